@@ -1,0 +1,11 @@
+"""fp64 CPU oracle for the attention path.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product library or its binding.
+"""
+
+from .attention import (apply_rope, attention, attention_rows, causal_mask, decode_paged,
+                        gather_paged, kv_head_of, max_abs, rel_rms, rope_inv_freq, sdpa)
+
+__all__ = ["apply_rope", "attention", "attention_rows", "causal_mask", "decode_paged",
+           "gather_paged", "kv_head_of", "max_abs", "rel_rms", "rope_inv_freq", "sdpa"]

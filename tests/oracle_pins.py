@@ -1,0 +1,440 @@
+"""Checks that pin the fp64 oracle to facts fixed by the pages and by mathematics.
+
+Each check takes an oracle module (the real one, or a copy with a planted
+mistake) and raises AssertionError when the fact does not hold.  The test
+files run every check against the real oracle, and run the whole battery
+against mutated copies to show that each plausible mistake fails at least one
+check.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+RNG_SEED = 1234
+
+
+def _rng(k=0):
+    return np.random.default_rng(RNG_SEED + k)
+
+
+# ------------------------------------------------------------------------
+# Pure-Python scalar brute force (no numpy, no broadcasting) of the
+# definition, used only for tiny shapes (T, S <= 8).
+# ------------------------------------------------------------------------
+
+def _bf_rotate(vec, p, base):
+    d = len(vec)
+    out = list(vec)
+    if base <= 0:
+        return out
+    for i in range(d // 2):
+        ang = p * base ** (-2.0 * i / d)
+        c, s = math.cos(ang), math.sin(ang)
+        a, b = vec[2 * i], vec[2 * i + 1]
+        out[2 * i] = a * c - b * s
+        out[2 * i + 1] = a * s + b * c
+    return out
+
+
+def brute_force_attention(q, k, v, causal, base, pos):
+    """q: nested lists [B][Hq][T][d]; k, v: [B][Hkv][S][d].  Returns (out, lse) as lists."""
+    B, Hq, T, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Hkv, S = len(k[0]), len(k[0][0])
+    group = Hq // Hkv
+    out = [[[None] * T for _ in range(Hq)] for _ in range(B)]
+    lse = [[[None] * T for _ in range(Hq)] for _ in range(B)]
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for t in range(T):
+                qt = _bf_rotate(q[b][h][t], pos + t, base)
+                logits = []
+                for s in range(S):
+                    if causal and s > pos + t:
+                        logits.append(None)
+                        continue
+                    ks = _bf_rotate(k[b][g][s], s, base)
+                    dot = 0.0
+                    for i in range(d):
+                        dot += qt[i] * ks[i]
+                    logits.append(dot / math.sqrt(d))
+                vis = [x for x in logits if x is not None]
+                if not vis:
+                    out[b][h][t] = [0.0] * d
+                    lse[b][h][t] = -math.inf
+                    continue
+                mx = max(vis)
+                e = [math.exp(x - mx) if x is not None else 0.0 for x in logits]
+                z = sum(e)
+                out[b][h][t] = [sum(e[s] * v[b][g][s][j] for s in range(S)) / z for j in range(d)]
+                lse[b][h][t] = mx + math.log(z)
+    return out, lse
+
+
+def check_bruteforce_tiny(orc, n_cases=40):
+    rng = _rng(1)
+    for case in range(n_cases):
+        T = int(rng.integers(1, 9))
+        S = int(rng.integers(1, 9))
+        Hq, Hkv = [(1, 1), (4, 2), (4, 1), (2, 2)][case % 4]
+        d = [2, 4, 6, 8][int(rng.integers(0, 4))]
+        causal = bool(case % 2)
+        base = [0.0, 10000.0, 7.0][case % 3]
+        pos = [0, 3][(case // 3) % 2]
+        if causal and pos + T - 1 < 0:
+            continue
+        q = rng.standard_normal((1, Hq, T, d))
+        k = rng.standard_normal((1, Hkv, S, d))
+        v = rng.standard_normal((1, Hkv, S, d))
+        o, l = orc.attention(q, k, v, causal=causal, rope_base=base, pos=pos)
+        bo, bl = brute_force_attention(q.tolist(), k.tolist(), v.tolist(), causal, base, pos)
+        bo = np.array(bo, dtype=np.float64)
+        bl = np.array(bl, dtype=np.float64)
+        assert o.shape == bo.shape, (case, o.shape, bo.shape)
+        assert np.allclose(o, bo, rtol=0, atol=1e-12), (case, np.max(np.abs(o - bo)))
+        fin = np.isfinite(bl)
+        assert np.array_equal(fin, np.isfinite(l))
+        assert np.allclose(l[fin], bl[fin], rtol=0, atol=1e-12), case
+
+
+# ------------------------------------------------------------------------
+# Closed forms and special cases.
+# ------------------------------------------------------------------------
+
+def check_q_zero_gives_mean(orc):
+    """Q = 0: every visible logit is 0, so O_t is the plain mean of the visible
+    values and lse_t = ln(#visible)."""
+    rng = _rng(2)
+    for causal in (False, True):
+        for (Hq, Hkv, T, S, pos, base) in [(4, 2, 7, 7, 0, 10000.0), (2, 1, 5, 9, 4, 0.0),
+                                           (3, 3, 6, 6, 0, 500000.0)]:
+            q = np.zeros((2, Hq, T, 8))
+            k = rng.standard_normal((2, Hkv, S, 8))
+            v = rng.standard_normal((2, Hkv, S, 8))
+            o, l = orc.attention(q, k, v, causal=causal, rope_base=base, pos=pos)
+            for b in range(2):
+                for h in range(Hq):
+                    g = h // (Hq // Hkv)
+                    for t in range(T):
+                        n = min(S, pos + t + 1) if causal else S
+                        assert np.allclose(o[b, h, t], v[b, g, :n].mean(axis=0), atol=1e-13)
+                        assert abs(l[b, h, t] - math.log(n)) < 1e-13
+
+
+def check_single_key(orc):
+    """T = S = 1: the output is v_0 and lse is the single scaled logit."""
+    rng = _rng(3)
+    for d in (2, 8, 64):
+        q = rng.standard_normal((1, 1, 1, d))
+        k = rng.standard_normal((1, 1, 1, d))
+        v = rng.standard_normal((1, 1, 1, d))
+        o, l = orc.attention(q, k, v, causal=True, rope_base=0.0)
+        assert np.allclose(o[0, 0, 0], v[0, 0, 0], atol=1e-14)
+        assert abs(l[0, 0, 0] - float(q[0, 0, 0] @ k[0, 0, 0]) / math.sqrt(d)) < 1e-12
+
+
+def check_causal_first_row(orc):
+    """Causal, pos = 0: query 0 sees only key 0 (and RoPE at position 0 is the identity)."""
+    rng = _rng(4)
+    q = rng.standard_normal((1, 2, 5, 8))
+    k = rng.standard_normal((1, 2, 5, 8))
+    v = rng.standard_normal((1, 2, 5, 8))
+    o, l = orc.attention(q, k, v, causal=True, rope_base=10000.0, pos=0)
+    for h in range(2):
+        assert np.allclose(o[0, h, 0], v[0, h, 0], atol=1e-14)
+        assert abs(l[0, h, 0] - float(q[0, h, 0] @ k[0, h, 0]) / math.sqrt(8)) < 1e-12
+
+
+def check_one_hot_logit_closed_form(orc):
+    """K = rows of the identity, q = a e_j: logit j is a/sqrt(d), the rest are 0, so
+    p_j = e^{a/sqrt d} / (e^{a/sqrt d} + S - 1) exactly, and lse = ln(e^{a/sqrt d} + S - 1)."""
+    rng = _rng(5)
+    d, S = 16, 12
+    k = np.eye(S, d)[None, None]
+    v = rng.standard_normal((1, 1, S, d))
+    for a in (0.5, 3.0, 40.0, 400.0, 6000.0):
+        for j in (0, 5, 11):
+            q = np.zeros((1, 1, 1, d))
+            q[0, 0, 0, j] = a
+            o, l = orc.attention(q, k, v)
+            z = a / math.sqrt(d)
+            pj = 1.0 / (1.0 + (S - 1) * math.exp(-z))
+            rest = np.delete(v[0, 0], j, axis=0).sum(axis=0)
+            want = pj * v[0, 0, j] + (1.0 - pj) / (S - 1) * rest
+            assert np.allclose(o[0, 0, 0], want, atol=1e-12), (a, j)
+            want_lse = z + math.log1p((S - 1) * math.exp(-z))
+            assert abs(l[0, 0, 0] - want_lse) < 1e-12, (a, j)
+
+
+def check_rope_d2_is_plane_rotation(orc):
+    """d_h = 2: one pair with frequency base^0 = 1, so RoPE is the plane rotation
+    by angle pos (complex multiplication by e^{i pos}; counter-clockwise reading)."""
+    rng = _rng(6)
+    x = rng.standard_normal((9, 2))
+    pos = np.array([0, 1, 2, 7, 100, 1000, 8191, 32767, 123456])
+    for base in (10000.0, 500000.0, 3.0):
+        y = orc.apply_rope(x, pos, base)
+        z = (x[:, 0] + 1j * x[:, 1]) * np.exp(1j * pos.astype(np.float64))
+        assert np.allclose(y[:, 0], z.real, atol=1e-9) and np.allclose(y[:, 1], z.imag, atol=1e-9)
+
+
+def check_rope_d4_frequencies(orc):
+    """d_h = 4: pair (0,1) turns by pos, pair (2,3) by pos / sqrt(base)
+    (theta = pos / base^(2i/d) with i = 1, d = 4)."""
+    rng = _rng(7)
+    x = rng.standard_normal((5, 4))
+    pos = np.array([0, 1, 5, 77, 4095])
+    for base in (10000.0, 16.0):
+        y = orc.apply_rope(x, pos, base)
+        for i, ang in ((0, pos.astype(np.float64)), (1, pos / math.sqrt(base))):
+            z = (x[:, 2 * i] + 1j * x[:, 2 * i + 1]) * np.exp(1j * ang)
+            assert np.allclose(y[:, 2 * i], z.real, atol=1e-10)
+            assert np.allclose(y[:, 2 * i + 1], z.imag, atol=1e-10)
+
+
+def check_rope_identity_at_zero(orc):
+    rng = _rng(8)
+    x = rng.standard_normal((1, 128))
+    assert np.array_equal(orc.apply_rope(x, np.array([0]), 10000.0), x)
+    assert np.array_equal(orc.apply_rope(x, np.array([5]), 0.0), x)
+
+
+def check_rope_relative_and_norm(orc):
+    """(R(m) q).(R(n) k) depends only on m - n; the rotation keeps norms."""
+    rng = _rng(9)
+    for base in (10000.0, 500000.0):
+        for d in (64, 128):
+            q = rng.standard_normal(d)
+            k = rng.standard_normal(d)
+            for (m, n) in ((5, 2), (100, 0), (4000, 3999)):
+                ref = float(orc.apply_rope(q[None], [m], base)[0] @ orc.apply_rope(k[None], [n], base)[0])
+                for c in (1, 17, 1000, 32767 - m):
+                    got = float(orc.apply_rope(q[None], [m + c], base)[0]
+                                @ orc.apply_rope(k[None], [n + c], base)[0])
+                    assert abs(got - ref) <= 1e-10 * max(1.0, abs(ref)), (base, d, m, n, c)
+            for p in (1, 33, 32767):
+                y = orc.apply_rope(q[None], [p], base)[0]
+                assert abs(np.linalg.norm(y) - np.linalg.norm(q)) < 1e-12
+                # each pair keeps its own norm
+                assert np.allclose(y[0::2] ** 2 + y[1::2] ** 2, q[0::2] ** 2 + q[1::2] ** 2, atol=1e-12)
+
+
+# ------------------------------------------------------------------------
+# Invariants.
+# ------------------------------------------------------------------------
+
+def check_rows_sum_to_one(orc):
+    """Masking on the logits before the softmax keeps each probability row summing to 1,
+    with zeros on hidden keys."""
+    rng = _rng(10)
+    q = rng.standard_normal((1, 2, 9, 8)) * 3
+    k = rng.standard_normal((1, 2, 9, 8)) * 3
+    v = rng.standard_normal((1, 2, 9, 8))
+    for causal in (False, True):
+        _, _, p = orc.attention(q, k, v, causal=causal, rope_base=10000.0, return_probs=True)
+        assert np.allclose(p.sum(axis=-1), 1.0, atol=1e-14)
+        assert np.all(p >= 0)
+        if causal:
+            assert np.all(np.triu(p[0, 0], 1) == 0)
+
+
+def check_permutation_equivariance(orc):
+    """Without positions or a mask: permuting the queries permutes the outputs, and a joint
+    permutation of keys and values changes nothing."""
+    rng = _rng(11)
+    q = rng.standard_normal((1, 1, 7, 8))
+    k = rng.standard_normal((1, 1, 10, 8))
+    v = rng.standard_normal((1, 1, 10, 8))
+    o, l = orc.attention(q, k, v)
+    pq = rng.permutation(7)
+    pk = rng.permutation(10)
+    o2, l2 = orc.attention(q[:, :, pq], k, v)
+    assert np.allclose(o2, o[:, :, pq], atol=1e-14) and np.allclose(l2, l[:, :, pq], atol=1e-14)
+    o3, l3 = orc.attention(q, k[:, :, pk], v[:, :, pk])
+    assert np.allclose(o3, o, atol=1e-13) and np.allclose(l3, l, atol=1e-13)
+
+
+def check_gqa_equals_repeated_mha(orc):
+    """Grouped-query attention equals multi-head attention with each KV head repeated for
+    its contiguous group of query heads."""
+    rng = _rng(12)
+    for (Hq, Hkv) in ((8, 2), (4, 1), (6, 3)):
+        q = rng.standard_normal((2, Hq, 5, 8))
+        k = rng.standard_normal((2, Hkv, 6, 8))
+        v = rng.standard_normal((2, Hkv, 6, 8))
+        o, l = orc.attention(q, k, v, causal=True, rope_base=10000.0, pos=1)
+        rep = Hq // Hkv
+        o2, l2 = orc.attention(q, np.repeat(k, rep, axis=1), np.repeat(v, rep, axis=1),
+                               causal=True, rope_base=10000.0, pos=1)
+        assert np.allclose(o, o2, atol=1e-14) and np.allclose(l, l2, atol=1e-14)
+        # and each query head depends only on its own KV head
+        k3 = k.copy()
+        k3[:, Hkv - 1] += 5.0
+        o3, _ = orc.attention(q, k3, v, causal=True, rope_base=10000.0, pos=1)
+        first = (Hkv - 1) * rep
+        assert np.allclose(o3[:, :first], o[:, :first], atol=1e-14)
+        assert not np.allclose(o3[:, first:], o[:, first:], atol=1e-6)
+
+
+def online_softmax_attention(qr, kr, v, mask, bounds):
+    """The blocked recurrence of the FlashAttention deep dive ("Why is attention O(n^2)..."):
+    running max m, normaliser l and unnormalised output o, rescaled by exp(m - m_new) per
+    key block; O = o / l at the end.  A row whose visible keys so far are none keeps m = -inf
+    (guarded so no NaN appears).  qr [T,d], kr [S,d], v [S,dv], mask [T,S] additive."""
+    T, d = qr.shape
+    m = np.full(T, -np.inf)
+    ell = np.zeros(T)
+    o = np.zeros((T, v.shape[1]))
+    for s0, s1 in bounds:
+        s = qr @ kr[s0:s1].T / math.sqrt(d) + mask[:, s0:s1]
+        m_new = np.maximum(m, s.max(axis=1))
+        m_use = np.where(np.isfinite(m_new), m_new, 0.0)
+        p = np.exp(s - m_use[:, None])
+        alpha = np.where(np.isfinite(m), np.exp(m - m_use), 0.0)
+        ell = alpha * ell + p.sum(axis=1)
+        o = alpha[:, None] * o + p @ v[s0:s1]
+        m = m_new
+    return o / ell[:, None], m + np.log(ell)
+
+
+def check_online_recurrence_equals_full(orc):
+    """The recurrence over arbitrary key-block partitions (including blocks that are fully
+    masked for some rows) gives the full softmax result up to rounding."""
+    rng = _rng(13)
+    for trial in range(12):
+        T = int(rng.integers(1, 40))
+        S = int(rng.integers(1, 60))
+        d = 16
+        pos = int(rng.integers(0, 5)) + max(0, S - T) * (trial % 2)
+        q = rng.standard_normal((1, 1, T, d)) * 2
+        k = rng.standard_normal((1, 1, S, d)) * 2
+        v = rng.standard_normal((1, 1, S, d))
+        base = 10000.0 if trial % 3 else 0.0
+        o, l = orc.attention(q, k, v, causal=True, rope_base=base, pos=pos)
+        cuts = sorted(set(rng.integers(1, S, size=int(rng.integers(0, 6))).tolist())) if S > 1 else []
+        bounds = list(zip([0] + cuts, cuts + [S]))
+        qr = orc.apply_rope(q[0, 0], pos + np.arange(T), base)
+        kr = orc.apply_rope(k[0, 0], np.arange(S), base)
+        mask = orc.causal_mask(pos + np.arange(T), np.arange(S))
+        o2, l2 = online_softmax_attention(qr, kr, v[0, 0], mask, bounds)
+        assert np.allclose(o2, o[0, 0], atol=1e-13), trial
+        assert np.allclose(l2, l[0, 0], atol=1e-13), trial
+
+
+def lse_merge(outs, lses):
+    """Combine normalised partial results over disjoint key sets: weights exp(lse_j - LSE)."""
+    lses = np.stack(lses)                      # [J, ...]
+    M = np.max(lses, axis=0)
+    w = np.exp(lses - M)
+    tot = np.sum(w, axis=0)
+    out = sum(w[j][..., None] * outs[j] for j in range(len(outs))) / tot[..., None]
+    return out, M + np.log(tot)
+
+
+def check_splitk_merge_equals_unsplit(orc):
+    rng = _rng(14)
+    for S in (5, 37, 100):
+        q = rng.standard_normal((3, 16)) * 2
+        k = rng.standard_normal((S, 16)) * 2
+        v = rng.standard_normal((S, 16))
+        o, l, _ = orc.sdpa(q, k, v)
+        cuts = sorted(set(rng.integers(1, S, size=3).tolist()))
+        parts = list(zip([0] + cuts, cuts + [S]))
+        outs, lses = [], []
+        for s0, s1 in parts:
+            oj, lj, _ = orc.sdpa(q, k[s0:s1], v[s0:s1])
+            outs.append(oj)
+            lses.append(lj)
+        o2, l2 = lse_merge(outs, lses)
+        assert np.allclose(o2, o, atol=1e-13) and np.allclose(l2, l, atol=1e-13)
+
+
+def _scatter_paged(rows, block_size, n_extra_blocks, rng, poison=np.nan):
+    """Place rows [Hkv, L, d] into a randomly permuted pool; unused slots get `poison`."""
+    Hkv, L, d = rows.shape
+    nb = (L + block_size - 1) // block_size
+    num_blocks = nb + n_extra_blocks
+    perm = rng.permutation(num_blocks)[:nb]
+    pool = np.full((num_blocks, Hkv, block_size, d), poison)
+    for j in range(L):
+        pool[perm[j // block_size], :, j % block_size, :] = rows[:, j, :]
+    table = perm.astype(np.int32)
+    return pool, table
+
+
+def check_gather_after_scatter_is_identity(orc):
+    rng = _rng(15)
+    for L in (1, 15, 16, 17, 100):
+        rows = rng.standard_normal((3, L, 8)).astype(np.float32)
+        pool, table = _scatter_paged(rows, 16, 3, rng)
+        got = orc.gather_paged(pool, table, L, 16)
+        assert got.dtype == pool.dtype and np.array_equal(got, rows.astype(pool.dtype))
+
+
+def check_decode_equals_last_causal_row(orc):
+    """A decode step over the paged cache (K stored already rotated) equals the last row of
+    causal prefill with RoPE on contiguous K."""
+    rng = _rng(16)
+    Hq, Hkv, d, bs = 4, 2, 8, 16
+    for L in (1, 16, 33, 70):
+        base = 10000.0
+        q_all = rng.standard_normal((1, Hq, L, d))
+        k = rng.standard_normal((1, Hkv, L, d))
+        v = rng.standard_normal((1, Hkv, L, d))
+        o, l = orc.attention(q_all, k, v, causal=True, rope_base=base, pos=0)
+        k_rot = orc.apply_rope(k[0], np.arange(L), base)
+        kpool, table = _scatter_paged(k_rot, bs, 2, np.random.default_rng(L))
+        vpool, table2 = _scatter_paged(v[0], bs, 2, np.random.default_rng(L))
+        assert np.array_equal(table, table2)
+        od, ld = orc.decode_paged(q_all[0, :, L - 1][None], kpool, vpool, table[None],
+                                  np.array([L]), bs, rope_base=base)
+        assert np.allclose(od[0], o[0, :, L - 1], atol=1e-13), L
+        assert np.allclose(ld[0], l[0, :, L - 1], atol=1e-13), L
+
+
+def check_torch_sdpa_core(orc):
+    """Library cross-check of scale, mask and GQA map: torch's fp64 CPU SDPA on the
+    oracle's rotated q and k must agree."""
+    rng = _rng(17)
+    for (Hq, Hkv, T, S, causal, pos) in ((4, 2, 9, 9, True, 0), (8, 2, 5, 12, False, 0),
+                                         (4, 4, 6, 10, True, 4)):
+        q = rng.standard_normal((2, Hq, T, 16))
+        k = rng.standard_normal((2, Hkv, S, 16))
+        v = rng.standard_normal((2, Hkv, S, 16))
+        base = 10000.0
+        o, l = orc.attention(q, k, v, causal=causal, rope_base=base, pos=pos)
+        qr = orc.apply_rope(q, pos + np.arange(T), base)
+        kr = orc.apply_rope(k, np.arange(S), base)
+        mask = None
+        if causal:
+            mask = torch.from_numpy(np.arange(S)[None, :] <= (pos + np.arange(T))[:, None])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qr), torch.from_numpy(kr), torch.from_numpy(v), attn_mask=mask,
+            enable_gqa=(Hq != Hkv)).numpy()
+        assert np.allclose(o, ref, atol=1e-12), np.max(np.abs(o - ref))
+
+
+def check_cross_attention_shapes(orc):
+    """T != S (cross-attention style): output has the query count and the value width; a
+    swap of queries and keys would change the shape."""
+    rng = _rng(18)
+    q = rng.standard_normal((1, 2, 3, 8))
+    k = rng.standard_normal((1, 2, 11, 8))
+    v = rng.standard_normal((1, 2, 11, 8))
+    o, l = orc.attention(q, k, v)
+    assert o.shape == (1, 2, 3, 8) and l.shape == (1, 2, 3)
+    o2, l2 = orc.attention_rows(q, k, v, [(0, 1, 2), (0, 0, 0)])
+    assert np.allclose(o2[0], o[0, 1, 2], atol=1e-14) and np.allclose(o2[1], o[0, 0, 0], atol=1e-14)
+
+
+ALL_CHECKS = [
+    check_bruteforce_tiny, check_q_zero_gives_mean, check_single_key, check_causal_first_row,
+    check_one_hot_logit_closed_form, check_rope_d2_is_plane_rotation, check_rope_d4_frequencies,
+    check_rope_identity_at_zero, check_rope_relative_and_norm, check_rows_sum_to_one,
+    check_permutation_equivariance, check_gqa_equals_repeated_mha,
+    check_online_recurrence_equals_full, check_splitk_merge_equals_unsplit,
+    check_gather_after_scatter_is_identity, check_decode_equals_last_causal_row,
+    check_torch_sdpa_core, check_cross_attention_shapes,
+]

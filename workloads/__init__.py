@@ -1,0 +1,123 @@
+"""Seeded synthetic workloads for the attention path.
+
+This module only draws random numbers and rounds them to the storage dtype.
+It holds none of the attention arithmetic, so both the fp64 oracle's tests and
+the HIP path's tests/bench can use it without sharing any method code.
+
+Workloads (shapes follow the typical figures the pages quote: 8-32 heads,
+head size 64-128, 4-8 KV heads for grouped-query attention, d = 4096; see
+"22 interview questions on attention & transformers", the multi-head and
+head-dimension answers, and "Transformer Attention Mechanism Interview Deep
+Dive", the variants table and the GQA paragraph after it):
+
+  small_f32    single-head non-causal fp32, T=S=128, d_h=64, no RoPE
+  mha2k        causal MHA prefill bf16, B=4, Hq=Hkv=32, T=S=2048, d_h=128, RoPE 1e4
+  gqa8k        causal GQA prefill bf16, B=2, Hq=32, Hkv=8, T=S=8192, RoPE 1e4
+  gqa32k       long-context causal GQA bf16, B=1, Hq=32, Hkv=8, T=S=32768,
+               sigma=0.5, RoPE 5e5 (past the T ~ 6d crossover for d=4096 that
+               "Why is attention O(n^2) ..." gives in its 30-second answer)
+  decode64     paged decode bf16, 64 sequences of one query token, context
+               lengths uniform in [512, 8192], Hq=32, Hkv=8, d_h=128, 16-token
+               blocks placed by a seeded random permutation of one pool
+
+Generation recipe: torch.Generator('cpu').manual_seed(seed); torch.randn in
+fp32 drawn in the order Q, K, V, multiplied by sigma, then rounded to the
+storage dtype with round-to-nearest-even (.to(torch.bfloat16)).
+"""
+
+
+import torch
+
+# name -> parameters.  "seed" is fixed per workload.
+CONFIGS = {
+    "small_f32": dict(kind="fwd", dtype="f32", B=1, Hq=1, Hkv=1, T=128, S=128, d_h=64,
+                      causal=False, rope_base=0.0, pos=0, sigma=1.0, seed=1),
+    "mha2k": dict(kind="fwd", dtype="bf16", B=4, Hq=32, Hkv=32, T=2048, S=2048, d_h=128,
+                  causal=True, rope_base=10000.0, pos=0, sigma=1.0, seed=2),
+    "gqa8k": dict(kind="fwd", dtype="bf16", B=2, Hq=32, Hkv=8, T=8192, S=8192, d_h=128,
+                  causal=True, rope_base=10000.0, pos=0, sigma=1.0, seed=3),
+    "gqa32k": dict(kind="fwd", dtype="bf16", B=1, Hq=32, Hkv=8, T=32768, S=32768, d_h=128,
+                   causal=True, rope_base=500000.0, pos=0, sigma=0.5, seed=4),
+    "decode64": dict(kind="decode", dtype="bf16", num_seqs=64, Hq=32, Hkv=8, d_h=128,
+                     block_size=16, len_lo=512, len_hi=8192, rope_base=10000.0,
+                     sigma=1.0, seed=5),
+}
+
+_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def torch_dtype(name):
+    return _TORCH_DTYPE[name]
+
+
+def make_fwd_inputs(B, Hq, Hkv, T, S, d_h, dtype="bf16", sigma=1.0, seed=0, **_):
+    """Q [B,Hq,T,d_h], K and V [B,Hkv,S,d_h], iid N(0, sigma^2), rounded to dtype (CPU tensors)."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    td = _TORCH_DTYPE[dtype]
+    q = (torch.randn((B, Hq, T, d_h), generator=g, dtype=torch.float32) * sigma).to(td)
+    k = (torch.randn((B, Hkv, S, d_h), generator=g, dtype=torch.float32) * sigma).to(td)
+    v = (torch.randn((B, Hkv, S, d_h), generator=g, dtype=torch.float32) * sigma).to(td)
+    return q, k, v
+
+
+def make_decode_inputs(num_seqs, Hq, Hkv, d_h, block_size=16, len_lo=512, len_hi=8192,
+                       dtype="bf16", sigma=1.0, seed=0, seq_lens=None, **_):
+    """Paged KV cache for one decode step.
+
+    Draw order: seq_lens = randint(len_lo, len_hi + 1) (inclusive range) unless given;
+    N = sum(ceil(L_b / block_size)) physical blocks; perm = randperm(N); sequence b
+    owns perm[off_b : off_b + ceil(L_b / block_size)] in order; unused table entries
+    are -1.  Then q [num_seqs,Hq,d_h], k_cache and v_cache [N,Hkv,block_size,d_h]
+    iid N(0, sigma^2), rounded to dtype.  Every slot of the pool is drawn, including
+    the slots past each sequence's length in its last block.
+    """
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    td = _TORCH_DTYPE[dtype]
+    if seq_lens is None:
+        seq_lens = torch.randint(len_lo, len_hi + 1, (num_seqs,), generator=g, dtype=torch.int64)
+    else:
+        seq_lens = torch.as_tensor(seq_lens, dtype=torch.int64)
+    nblk = [(int(L) + block_size - 1) // block_size for L in seq_lens.tolist()]
+    num_blocks = sum(nblk)
+    max_blocks = max(nblk) if nblk else 0
+    perm = torch.randperm(num_blocks, generator=g)
+    block_table = torch.full((num_seqs, max(max_blocks, 1)), -1, dtype=torch.int32)
+    off = 0
+    for b, n in enumerate(nblk):
+        block_table[b, :n] = perm[off:off + n].to(torch.int32)
+        off += n
+    q = (torch.randn((num_seqs, Hq, d_h), generator=g, dtype=torch.float32) * sigma).to(td)
+    k_cache = (torch.randn((num_blocks, Hkv, block_size, d_h), generator=g,
+                           dtype=torch.float32) * sigma).to(td)
+    v_cache = (torch.randn((num_blocks, Hkv, block_size, d_h), generator=g,
+                           dtype=torch.float32) * sigma).to(td)
+    return dict(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                seq_lens=seq_lens.to(torch.int32), block_size=block_size,
+                num_blocks=num_blocks, max_blocks_per_seq=block_table.shape[1])
+
+
+def fwd_flops(B, Hq, T, S, d_h, causal, **_):
+    """Algorithmic FLOPs of one forward: 4*B*Hq*T*S*d_h, halved when causal."""
+    f = 4.0 * B * Hq * T * S * d_h
+    return f / 2.0 if causal else f
+
+
+def decode_kv_bytes(seq_lens, Hkv, d_h, elem_bytes=2):
+    """KV bytes a decode step must read: sum_b L_b * Hkv * d_h * 2 (K and V) * elem_bytes."""
+    return int(sum(int(L) for L in seq_lens)) * Hkv * d_h * 2 * elem_bytes
+
+
+def fwd_io_bytes(B, Hq, Hkv, T, S, d_h, elem_bytes=2, **_):
+    """Compulsory HBM bytes of one forward: read Q, K, V once, write O and the fp32 lse."""
+    return elem_bytes * (2 * B * Hq * T * d_h + 2 * B * Hkv * S * d_h) + 4 * B * Hq * T
+
+
+def scaled(cfg, **overrides):
+    """Copy of a workload's parameters with some fields replaced (smaller test shapes)."""
+    c = dict(cfg)
+    c.update(overrides)
+    return c
+
+
+__all__ = ["CONFIGS", "make_fwd_inputs", "make_decode_inputs", "fwd_flops", "decode_kv_bytes",
+           "fwd_io_bytes", "scaled", "torch_dtype"]
