@@ -1,0 +1,136 @@
+// Host entry points of libattn: argument validation, parameter packing and launch.
+// Every check runs before the first HIP call, so an invalid request leaves the stream
+// untouched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "../../include/attn.h"
+#include "launchers.h"
+
+namespace {
+
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+
+// rope_c[i] = base^(-2i/d_h) / (2 pi): turns of rotation per position for pair i
+// ("How does Rotary Position Embedding (RoPE) work?": theta = pos / base^(2i/d)).
+void fill_rope(double* c, int d_h, float base) {
+  for (int i = 0; i < d_h / 2; ++i)
+    c[i] = std::pow((double)base, -2.0 * (double)i / (double)d_h) / kTwoPi;
+  for (int i = d_h / 2; i < attn::kMaxHalfDim; ++i) c[i] = 0.0;
+}
+
+bool bad_base(float rope_base) { return !(std::isfinite(rope_base) && rope_base >= 0.f); }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+                       int Hkv, int T, int S, int d_h, int causal, float rope_base, int64_t pos,
+                       attn_dtype_t dtype, void* stream) {
+  if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || d_h < 1) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (bad_base(rope_base)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (d_h != 64 && d_h != 128) return ATTN_ERR_UNSUPPORTED;
+  if (pos > ((int64_t)1 << 40) || pos < -((int64_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
+
+  attn::FwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.T = T;
+  p.S = S;
+  p.causal = causal;
+  p.pos = pos;
+  p.use_rope = rope_base > 0.f;
+  fill_rope(p.rope_c, d_h, p.use_rope ? rope_base : 1.f);
+
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = (dtype == ATTN_F32) ? attn::launch_fwd_f32(p, d_h, st) : attn::launch_fwd_bf16(p, d_h, st);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int d_h, int max_blocks_per_seq, int block_size) {
+  if (num_seqs < 1 || Hq < 1 || d_h < 1 || max_blocks_per_seq < 1 || block_size < 1) return 0;
+  const int bps = attn::decode_blocks_per_split(max_blocks_per_seq);
+  const size_t splits = (size_t)((max_blocks_per_seq + bps - 1) / bps);
+  return (size_t)num_seqs * (size_t)Hq * splits * ((size_t)d_h + 2) * sizeof(float);
+}
+
+attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                                int num_seqs, int Hq, int Hkv, int d_h, int max_blocks_per_seq,
+                                int num_blocks, float rope_base, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return ATTN_ERR_INVALID_ARG;
+  if (num_seqs < 1 || Hq < 1 || Hkv < 1 || d_h < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      block_size < 1)
+    return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (bad_base(rope_base)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16 || d_h != 128 || block_size != 16 || Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn_decode_workspace_bytes(num_seqs, Hq, d_h, max_blocks_per_seq, block_size);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+
+  attn::DecodeParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.lse = lse;
+  p.num_seqs = num_seqs;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.blocks_per_split = attn::decode_blocks_per_split(max_blocks_per_seq);
+  p.max_splits = (max_blocks_per_seq + p.blocks_per_split - 1) / p.blocks_per_split;
+  const size_t nparts = (size_t)num_seqs * Hq * p.max_splits;
+  p.part_o = (float*)workspace;
+  p.part_ml = (float*)workspace + nparts * d_h;
+  p.use_rope = rope_base > 0.f;
+  fill_rope(p.rope_c, d_h, p.use_rope ? rope_base : 1.f);
+  hipError_t e = attn::launch_decode_paged(p, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t attn_paged_gather(const void* cache, const int32_t* block_table, const int32_t* seq_lens,
+                                int block_size, int num_seqs, int Hkv, int d_h, int max_blocks_per_seq,
+                                int num_blocks, int elem_bytes, void* dst, void* stream) {
+  if (!cache || !block_table || !seq_lens || !dst) return ATTN_ERR_INVALID_ARG;
+  if (num_seqs < 1 || Hkv < 1 || d_h < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || block_size < 1)
+    return ATTN_ERR_INVALID_ARG;
+  if (elem_bytes != 2 && elem_bytes != 4) return ATTN_ERR_INVALID_ARG;
+  if (block_size != 16 || (d_h * elem_bytes) % 64 != 0) return ATTN_ERR_UNSUPPORTED;
+  hipError_t e = attn::launch_paged_gather(cache, block_table, seq_lens, num_seqs, Hkv, d_h,
+                                           max_blocks_per_seq, elem_bytes, dst, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,27 @@
+// Launch parameters shared by the prefill kernels and the host entry point.
+#pragma once
+
+#include <stdint.h>
+
+namespace attn {
+
+constexpr int kMaxHalfDim = 64;  // d_h <= 128
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;  // may be null
+  int B, Hq, Hkv, T, S;
+  int causal;
+  int use_rope;
+  int n_qblocks;  // query blocks per (batch, head group)
+  int n_groups;   // batch * head groups
+  int xcd_remap;  // 1 if n_groups is a multiple of 8 (see work mapping in the kernel)
+  int64_t pos;
+  // RoPE: rope_c[i] = rope_base^(-2i/d_h) / (2 pi), i = 0..d_h/2-1 (turns per position).
+  double rope_c[kMaxHalfDim];
+};
+
+}  // namespace attn

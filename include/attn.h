@@ -1,0 +1,133 @@
+/*
+ * libattn -- exact scaled dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument is caller-owned device memory (or NULL where a
+ * parameter says it may be); the library allocates nothing and keeps no state
+ * between calls.  Every call validates its arguments on the host before any HIP
+ * call and, on error, returns a status without touching the stream.  On success
+ * the work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ * void*; NULL means the null stream) and the call returns ATTN_OK once the
+ * launches were accepted.  A launch failure reported by the HIP runtime returns
+ * ATTN_ERR_HIP.  Calls are thread-safe.  Outputs must not alias inputs.
+ *
+ * Layouts are dense row-major:
+ *   prefill  q, out [B, Hq, T, d_h];  k, v [B, Hkv, S, d_h];  lse [B, Hq, T] fp32
+ *   decode   q, out [num_seqs, Hq, d_h];  k_cache, v_cache [num_blocks, Hkv, block_size, d_h]
+ *            block_table [num_seqs, max_blocks_per_seq] int32;  seq_lens [num_seqs] int32;
+ *            lse [num_seqs, Hq] fp32
+ * out has the dtype of the inputs; accumulation and lse are fp32.
+ */
+#ifndef LIBATTN_ATTN_H
+#define LIBATTN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_API __attribute__((visibility("default")))
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,  /* NULL pointer, non-positive size, Hq % Hkv != 0, bad table size */
+  ATTN_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (d_h, dtype, block_size) */
+  ATTN_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than attn_decode_workspace_bytes() */
+  ATTN_ERR_HIP = 4           /* the HIP runtime rejected a launch */
+} attn_status_t;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/*
+ * attn_fwd -- exact attention softmax(Q K^T / sqrt(d_h)) V over whole sequences
+ * ("22 interview questions on attention & transformers", How does self-attention
+ * work; "Transformer Attention Mechanism Interview Deep Dive", Scaled dot-product
+ * attention), computed with the blocked online softmax of "Why is attention O(n^2),
+ * how does FlashAttention help ..." (Deep dive: FlashAttention): the T x S score
+ * matrix is never written to memory.
+ *
+ *   q        [B, Hq, T, d_h]   queries, dtype `dtype`
+ *   k, v     [B, Hkv, S, d_h]  keys and values; query head h reads KV head
+ *                              h / (Hq / Hkv) (grouped-query sharing, contiguous groups)
+ *   out      [B, Hq, T, d_h]   result, dtype `dtype`
+ *   lse      [B, Hq, T] fp32 or NULL: natural log of the sum over visible keys of
+ *                              exp(q.k / sqrt(d_h)) (the saved statistic a backward
+ *                              pass recomputes probabilities from); -inf for a row
+ *                              with no visible key
+ *   causal   0 or 1: key s is visible to query row t iff s <= pos + t; hidden logits
+ *            are -inf before the softmax ("Causal masking" of the Deep Dive page), and
+ *            key blocks hidden from every row of a query block are skipped
+ *   rope_base  > 0: rotate q and k at load, adjacent pairs (2i, 2i+1) by the angle
+ *            position * rope_base^(-2i/d_h) ("How does Rotary Position Embedding (RoPE)
+ *            work?"); query row t sits at position pos + t, key s at position s.
+ *            0 disables the rotation.
+ *   pos      absolute position of query row 0 (0 for self-attention over a prompt)
+ *   dtype    ATTN_F32 or ATTN_BF16 (bf16 inputs use bf16 MFMA with fp32 accumulation)
+ *
+ * Supported: d_h in {64, 128}; any B, Hq, Hkv >= 1 with Hq % Hkv == 0; any
+ * T, S >= 1 (ragged tails are masked).  The 1/sqrt(d_h) scale is fixed.
+ */
+ATTN_API attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int B, int Hq, int Hkv, int T, int S, int d_h, int causal,
+                       float rope_base, int64_t pos, attn_dtype_t dtype, void* stream);
+
+/*
+ * attn_decode_paged -- one decode step over a block-tabled KV cache ("Self-Attention
+ * Complexity, FlashAttention, PagedAttention, and RoPE in Code", Part 3: fixed-size
+ * blocks and per-sequence block tables; "Why is attention O(n^2) ...": a decode step
+ * attends to every cached key and is memory-bound).
+ *
+ *   q            [num_seqs, Hq, d_h]  the one new query token of each sequence; it is
+ *                rotated at position seq_lens[b] - 1 when rope_base > 0
+ *   k_cache, v_cache  [num_blocks, Hkv, block_size, d_h]  physical block pool; cached K
+ *                is used as stored (already rotated at its own position)
+ *   block_table  [num_seqs, max_blocks_per_seq] int32: token j of sequence b lives in
+ *                slot j % block_size of physical block block_table[b][j / block_size];
+ *                entries past the sequence are ignored
+ *   seq_lens     [num_seqs] int32: cached tokens per sequence (current one included);
+ *                device contract: 1 <= seq_lens[b] <= max_blocks_per_seq * block_size and
+ *                every used table entry in [0, num_blocks) (not checked on the device)
+ *   out          [num_seqs, Hq, d_h] dtype `dtype`;  lse [num_seqs, Hq] fp32 or NULL
+ *   workspace    device scratch of at least attn_decode_workspace_bytes(...) bytes for
+ *                the split-K partial results; caller-owned, contents need no clearing
+ *   dtype        ATTN_BF16 only (ATTN_F32 returns ATTN_ERR_UNSUPPORTED)
+ *
+ * Supported: block_size == 16, d_h == 128, Hq % Hkv == 0, Hq / Hkv <= 16.
+ * The key range of each (sequence, KV head) is cut into splits that run in parallel;
+ * a second kernel merges the partial (output, max, normaliser) triples with a
+ * log-sum-exp merge.
+ */
+ATTN_API attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int block_size, int num_seqs, int Hq, int Hkv, int d_h,
+                                int max_blocks_per_seq, int num_blocks, float rope_base,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                attn_dtype_t dtype, void* stream);
+
+/* Bytes of workspace attn_decode_paged needs for these sizes (0 on invalid sizes). */
+ATTN_API size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int d_h, int max_blocks_per_seq,
+                                   int block_size);
+
+/*
+ * attn_paged_gather -- copy each sequence's cached rows into a contiguous buffer using
+ * the same block-table address code as attn_decode_paged (an exact copy; it exists so
+ * that the address translation can be checked bit for bit).
+ *
+ *   cache        [num_blocks, Hkv, block_size, d_h] elements of elem_bytes (2 or 4)
+ *   dst          [num_seqs, Hkv, max_blocks_per_seq * block_size, d_h]; rows j >= seq_lens[b]
+ *                are left untouched
+ */
+ATTN_API attn_status_t attn_paged_gather(const void* cache, const int32_t* block_table,
+                                const int32_t* seq_lens, int block_size, int num_seqs, int Hkv,
+                                int d_h, int max_blocks_per_seq, int num_blocks, int elem_bytes,
+                                void* dst, void* stream);
+
+/* Static description of a status code. */
+ATTN_API const char* attn_status_str(attn_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_ATTN_H */

@@ -1,0 +1,103 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the header
+declares, and rejects invalid requests on the host before touching HIP."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"ATTN_API\s+[\w\s\*]*?\b(attn_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import exact_transformer_attention_amd as e
+    return e.LIB
+
+
+def test_header_declares_entry_points():
+    names = header_functions()
+    assert names == sorted(["attn_fwd", "attn_decode_paged", "attn_decode_workspace_bytes",
+                            "attn_paged_gather", "attn_status_str"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    # and the exported dynamic symbol table holds exactly those attn_ entry points
+    import subprocess
+    import exact_transformer_attention_amd as e
+    out = subprocess.run(["nm", "-D", "--defined-only", e.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r"\bT (attn_\w+)", out)))
+    assert exported == header_functions()
+
+
+def test_status_strings(lib):
+    import exact_transformer_attention_amd as e
+    assert e.attn_status_str(e.ATTN_OK) == "ok"
+    for s in range(1, 5):
+        assert e.attn_status_str(s) != "ok"
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, B=1, Hq=4, Hkv=2, T=8, S=8, d=128, causal=1,
+             base=10000.0, pos=0, dtype=1)
+    a.update(kw)
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["T"], a["S"],
+                        a["d"], a["causal"], a["base"], a["pos"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(out=None), 1),
+    (dict(B=0), 1), (dict(Hq=0), 1), (dict(Hkv=0), 1), (dict(T=0), 1), (dict(S=-1), 1), (dict(d=0), 1),
+    (dict(Hq=6, Hkv=4), 1), (dict(causal=2), 1), (dict(base=-1.0), 1), (dict(base=float("nan")), 1),
+    (dict(base=float("inf")), 1), (dict(dtype=7), 1),
+    (dict(d=96), 2), (dict(d=256), 2), (dict(pos=1 << 41), 2),
+])
+def test_fwd_validation(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+def dec(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, bs=16, N=4, Hq=32, Hkv=8, d=128, mbps=10, nb=40,
+             base=10000.0, out=FAKE, lse=None, ws=FAKE, wsb=1 << 30, dtype=1)
+    a.update(kw)
+    return lib.attn_decode_paged(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["bs"], a["N"], a["Hq"], a["Hkv"],
+                                 a["d"], a["mbps"], a["nb"], a["base"], a["out"], a["lse"], a["ws"], a["wsb"],
+                                 a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(kc=None), 1), (dict(bt=None), 1), (dict(sl=None), 1), (dict(out=None), 1),
+    (dict(N=0), 1), (dict(Hq=30), 1), (dict(mbps=0), 1), (dict(nb=0), 1), (dict(bs=0), 1),
+    (dict(base=-2.0), 1), (dict(dtype=5), 1),
+    (dict(dtype=0), 2), (dict(d=64), 2), (dict(bs=32), 2), (dict(Hq=64, Hkv=2), 2),
+    (dict(ws=None), 3), (dict(wsb=16), 3),
+])
+def test_decode_validation(lib, kw, status):
+    assert dec(lib, **kw) == status
+
+
+def test_workspace_bytes(lib):
+    import exact_transformer_attention_amd as e
+    # 32 blocks (512 tokens) per split: 512 blocks -> 16 splits; (d_h + 2) fp32 per partial
+    assert e.attn_decode_workspace_bytes(64, 32, 128, 512, 16) == 64 * 32 * 16 * 130 * 4
+    assert e.attn_decode_workspace_bytes(1, 1, 128, 1, 16) == 130 * 4
+    assert e.attn_decode_workspace_bytes(0, 32, 128, 512, 16) == 0
+
+
+def test_gather_validation(lib):
+    f = lib.attn_paged_gather
+    assert f(None, FAKE, FAKE, 16, 1, 1, 128, 1, 1, 2, FAKE, None) == 1
+    assert f(FAKE, FAKE, FAKE, 16, 1, 1, 128, 1, 1, 3, FAKE, None) == 1
+    assert f(FAKE, FAKE, FAKE, 8, 1, 1, 128, 1, 1, 2, FAKE, None) == 2

@@ -1,0 +1,113 @@
+"""Prefill parity: libattn's attn_fwd (HIP, through the C ABI) against the fp64 oracle on
+the same seeded inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_common import check_close, f64, gen, run_fwd_gpu, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def full_case(dtype, B, Hq, Hkv, T, S, d_h, causal, rope_base, pos, seed, sigma=1.0):
+    cfg = dict(B=B, Hq=Hq, Hkv=Hkv, T=T, S=S, d_h=d_h, dtype=dtype, sigma=sigma, seed=seed)
+    say(f"case {cfg} causal={causal} rope={rope_base} pos={pos}")
+    q, k, v = gen(cfg)
+    out, lse = run_fwd_gpu(q, k, v, causal, rope_base, pos)
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), causal=causal, rope_base=rope_base, pos=pos)
+    check_close(f64(out), ro, dtype, "out", f64(lse), rl)
+
+
+# ---------------------------------------------------------------- fp32 ----
+
+def test_small_f32_workload():
+    cfg = workloads.CONFIGS["small_f32"]
+    full_case("f32", cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], cfg["S"], cfg["d_h"], cfg["causal"],
+              cfg["rope_base"], cfg["pos"], cfg["seed"])
+
+
+F32_CASES = [
+    # B, Hq, Hkv, T, S, d_h, causal, rope_base, pos
+    (1, 1, 1, 1, 1, 64, False, 0.0, 0),
+    (1, 2, 1, 33, 33, 64, True, 10000.0, 0),
+    (2, 4, 2, 100, 100, 128, True, 10000.0, 0),
+    (1, 3, 1, 70, 150, 128, False, 500000.0, 0),
+    (1, 2, 2, 40, 200, 64, True, 10000.0, 160),
+    (1, 8, 2, 129, 129, 128, False, 0.0, 0),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_f32_shapes(case):
+    B, Hq, Hkv, T, S, d, causal, base, pos = case
+    full_case("f32", B, Hq, Hkv, T, S, d, causal, base, pos, seed=100 + T)
+
+
+# ---------------------------------------------------------------- bf16 ----
+
+BF16_CASES = [
+    # several 64-key blocks and a ragged tail, every GQA packing (1, 2, 4 heads per KV head and
+    # a group of 3), both head sizes, causal and not, RoPE and not, T != S and pos != 0
+    (1, 4, 4, 200, 200, 128, True, 10000.0, 0),
+    (1, 4, 1, 200, 200, 128, True, 10000.0, 0),
+    (1, 4, 2, 200, 200, 128, False, 10000.0, 0),
+    (2, 6, 2, 130, 130, 128, True, 500000.0, 0),
+    (1, 8, 2, 300, 300, 64, True, 10000.0, 0),
+    (1, 2, 1, 77, 300, 128, False, 0.0, 0),
+    (1, 4, 1, 64, 320, 128, True, 10000.0, 256),
+    (1, 2, 2, 1, 1, 128, True, 10000.0, 0),
+    (1, 4, 4, 1, 500, 128, True, 10000.0, 499),
+    (1, 1, 1, 257, 257, 128, True, 10000.0, 0),
+    (1, 4, 1, 520, 520, 128, True, 10000.0, 0),
+    (1, 16, 2, 96, 96, 64, False, 0.0, 0),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bf16_shapes(case):
+    B, Hq, Hkv, T, S, d, causal, base, pos = case
+    full_case("bf16", B, Hq, Hkv, T, S, d, causal, base, pos, seed=200 + T + S)
+
+
+def test_bf16_fully_masked_rows():
+    """pos < 0 with causal leaves the first rows without any visible key: output 0, lse -inf."""
+    cfg = dict(B=1, Hq=4, Hkv=1, T=100, S=100, d_h=128, dtype="bf16", seed=7)
+    q, k, v = gen(cfg)
+    for dtype in ("bf16", "f32"):
+        qq, kk, vv = (x.float() for x in (q, k, v)) if dtype == "f32" else (q, k, v)
+        out, lse = run_fwd_gpu(qq, kk, vv, True, 10000.0, -5)
+        ro, rl = oracle.attention(f64(qq), f64(kk), f64(vv), causal=True, rope_base=10000.0, pos=-5)
+        o = f64(out)
+        assert np.all(o[:, :, :5] == 0) and np.all(np.isneginf(f64(lse)[:, :, :5]))
+        check_close(o, ro, dtype, f"masked rows {dtype}", f64(lse), rl)
+
+
+def test_bf16_deterministic():
+    cfg = dict(B=1, Hq=8, Hkv=2, T=300, S=300, d_h=128, dtype="bf16", seed=8)
+    q, k, v = gen(cfg)
+    a = run_fwd_gpu(q, k, v, True, 10000.0, 0)
+    b = run_fwd_gpu(q, k, v, True, 10000.0, 0)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------- full workloads ----
+
+@pytest.mark.parametrize("name", ["mha2k", "gqa8k", "gqa32k"])
+def test_full_workload_sampled_rows(name):
+    """Each full-size workload in the launch configuration the benchmark times; the oracle
+    evaluates a sample of rows (first/last rows of several heads plus random rows)."""
+    cfg = workloads.CONFIGS[name]
+    say(f"workload {name}: {cfg}")
+    q, k, v = gen(cfg)
+    out, lse = run_fwd_gpu(q, k, v, cfg["causal"], cfg["rope_base"], cfg["pos"])
+    assert bool(torch.isfinite(out).all()), "non-finite output"
+    rows = sample_rows(cfg["B"], cfg["Hq"], cfg["T"], 160, seed=cfg["seed"])
+    ro, rl = oracle.attention_rows(f64(q), f64(k), f64(v), rows,
+                                   causal=cfg["causal"], rope_base=cfg["rope_base"], pos=cfg["pos"])
+    idx = (rows[:, 0], rows[:, 1], rows[:, 2])
+    got = f64(out)[idx]
+    got_lse = f64(lse)[idx]
+    check_close(got, ro, "bf16", f"{name} sampled rows", got_lse, rl)
