@@ -1,0 +1,240 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one causal GQA prefill (B=2, Hq=32, Hkv=8, T=S=8192, d_h=128, bf16, RoPE 1e4;
+attn_fwd) followed by one paged decode step (64 sequences, lengths uniform in
+[512, 8192], Hq=32, Hkv=8, block 16; attn_decode_paged), on synthetic seeded inputs
+already resident in HBM.
+
+Prints one JSON line.  value = prefill TFLOP/s (4*B*Hq*T*S*d_h, halved for causal)
+measured with HIP events on the stream the kernels run on; the decode step is reported
+beside it in KV bytes read per second (sum_b L_b*Hkv*d_h*2*2 bytes).  Each comes with
+its roofline fraction (bf16 dense MFMA 2516.6 TFLOP/s; HBM 8 TB/s) and the fp64 oracle
+timed on the host cores on a bounded sample.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0          # HBM3E
+
+
+def kernel_sources_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ["exact_transformer_attention_amd/csrc/fwd_bf16.hip",
+                   "exact_transformer_attention_amd/csrc/attn_common.h",
+                   "exact_transformer_attention_amd/csrc/fwd_params.h"]
+DECODE_SOURCES = ["exact_transformer_attention_amd/csrc/decode.hip",
+                  "exact_transformer_attention_amd/csrc/attn_common.h",
+                  "exact_transformer_attention_amd/csrc/launchers.h"]
+
+
+def measured_traffic(kind, digest):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was taken on
+    the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f).get(kind)
+    if not t or t.get("source_digest") != digest:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_prefill(cfg):
+    """The fp64 oracle on a bounded sample of the prefill workload: batch 0, the 8 query
+    heads of KV heads 0 and 1, all 8192 rows (row blocks of 1024, each with its full softmax)."""
+    import numpy as np
+    import oracle
+    import workloads
+    q, k, v = workloads.make_fwd_inputs(**cfg)
+    qs = q[:1, :8].double().numpy()
+    ks = k[:1, :2].double().numpy()
+    vs = v[:1, :2].double().numpy()
+    t0 = time.perf_counter()
+    oracle.attention(qs, ks, vs, causal=cfg["causal"], rope_base=cfg["rope_base"], pos=cfg["pos"],
+                     row_block=1024)
+    dt = time.perf_counter() - t0
+    flops = workloads.fwd_flops(1, 8, cfg["T"], cfg["S"], cfg["d_h"], cfg["causal"])
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cpu_threads(), kind="oracle",
+                seconds=round(dt, 3),
+                sample=f"batch 0, query heads 0-7 (KV heads 0-1), all {cfg['T']} rows x {cfg['S']} keys, "
+                       f"fp64 numpy, 1024-row blocks; {flops:.3e} algorithmic FLOP")
+
+
+def cpu_baseline_decode(d, cfg, n_seqs=8):
+    """The fp64 oracle on the first n_seqs sequences of the decode workload."""
+    import oracle
+    import workloads
+    sl = d["seq_lens"][:n_seqs].numpy()
+    kc, vc = d["k_cache"].float().numpy(), d["v_cache"].float().numpy()   # bf16 values, exact in fp32
+    t0 = time.perf_counter()
+    oracle.decode_paged(d["q"][:n_seqs].double().numpy(), kc, vc,
+                        d["block_table"][:n_seqs].numpy(), sl, d["block_size"], rope_base=cfg["rope_base"])
+    dt = time.perf_counter() - t0
+    nbytes = workloads.decode_kv_bytes(sl, cfg["Hkv"], cfg["d_h"])
+    return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=cpu_threads(), kind="oracle", seconds=round(dt, 3),
+                sample=f"first {n_seqs} of {cfg['num_seqs']} sequences ({int(sl.sum())} tokens), fp64 numpy")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time only one part (profiling runs)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the kernels are "
+              "single-GPU and no multi-GPU path is built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from exact_transformer_attention_amd import attn_decode_paged, attn_fwd
+
+    dev = torch.device("cuda:0")
+    pcfg = workloads.CONFIGS["gqa8k"]
+    dcfg = workloads.CONFIGS["decode64"]
+    print(f"[bench] generating inputs", file=sys.stderr, flush=True)
+    q, k, v = workloads.make_fwd_inputs(**pcfg)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    d = workloads.make_decode_inputs(**dcfg)
+    dq = d["q"].to(dev)
+    dk, dv = d["k_cache"].to(dev), d["v_cache"].to(dev)
+    dbt, dsl = d["block_table"].to(dev), d["seq_lens"].to(dev)
+    dout = torch.empty_like(dq)
+    dlse = torch.empty(dq.shape[:2], dtype=torch.float32, device=dev)
+    from exact_transformer_attention_amd import attn_decode_workspace_bytes
+    ws = torch.empty(attn_decode_workspace_bytes(dcfg["num_seqs"], dcfg["Hq"], dcfg["d_h"],
+                                                 d["max_blocks_per_seq"], 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    do_p = a.only in (None, "prefill")
+    do_d = a.only in (None, "decode")
+
+    def prefill():
+        attn_fwd(qd, kd, vd, causal=pcfg["causal"], rope_base=pcfg["rope_base"], pos=pcfg["pos"], out=out,
+                 lse=lse)
+
+    def decode():
+        attn_decode_paged(dq, dk, dv, dbt, dsl, block_size=16, rope_base=dcfg["rope_base"], out=dout,
+                          lse=dlse, workspace=ws)
+
+    print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        if do_p:
+            prefill()
+        if do_d:
+            decode()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(a.steps):
+        ev[i][0].record(stream)
+        if do_p:
+            prefill()
+        ev[i][1].record(stream)
+        if do_d:
+            decode()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    p_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(a.steps)]
+    d_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(a.steps)]
+    p_avg = sum(p_ms) / len(p_ms)
+    d_avg = sum(d_ms) / len(d_ms)
+    print(f"[bench] prefill ms avg {p_avg:.4f} min {min(p_ms):.4f}; decode ms avg {d_avg:.4f} "
+          f"min {min(d_ms):.4f}; wall {wall:.3f}s", file=sys.stderr, flush=True)
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(dout).all())
+
+    if a.copy_calibration:
+        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+
+    flops = workloads.fwd_flops(**pcfg)
+    tflops = flops / (p_avg * 1e-3) / 1e12 if do_p else 0.0
+    kv_bytes = workloads.decode_kv_bytes(d["seq_lens"].tolist(), dcfg["Hkv"], dcfg["d_h"])
+    dec_gbs = kv_bytes / (d_avg * 1e-3) / 1e9 if do_d else 0.0
+
+    res = {
+        "metric": "attention fwd TFLOP/s + % bf16 MFMA peak; paged-decode KV GB/s + % HBM peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(p_avg + d_avg, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid normal, bf16-rounded)",
+        "config": {
+            "workload": "causal GQA prefill B=2 Hq=32 Hkv=8 T=S=8192 d_h=128 RoPE 1e4 "
+                        "+ paged decode 64 seqs L~U[512,8192] Hq=32 Hkv=8 d_h=128 block 16",
+            "prefill": {k_: pcfg[k_] for k_ in ("B", "Hq", "Hkv", "T", "S", "d_h", "causal", "rope_base")},
+            "decode": {"num_seqs": dcfg["num_seqs"], "Hq": dcfg["Hq"], "Hkv": dcfg["Hkv"], "d_h": dcfg["d_h"],
+                       "block_size": 16, "total_tokens": int(d["seq_lens"].sum()), "kv_bytes": kv_bytes},
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("prefill", kernel_sources_digest(PREFILL_SOURCES)),
+            "kernel": "fwd_bf16_kernel<128,4>", "flop_per_launch": flops, "avg_launch_ms": round(p_avg, 4),
+        },
+        "decode": {
+            "value": round(dec_gbs, 1), "unit": "GB/s", "avg_step_ms": round(d_avg, 4),
+            "roofline": {
+                "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic("decode", kernel_sources_digest(DECODE_SOURCES)),
+                "kernels": "decode_partial_kernel + decode_merge_kernel", "kv_bytes_per_launch": kv_bytes,
+            },
+        },
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the oracle on the host (prefill sample)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_prefill(pcfg)
+        print("[bench] timing the oracle on the host (decode sample)", file=sys.stderr, flush=True)
+        res["decode"]["cpu_baseline"] = cpu_baseline_decode(d, dcfg)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,6 +18,10 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
 SOURCES = ["api.cpp", "fwd_f32.hip", "fwd_bf16.hip", "decode.hip"]
+# Per-source extra flags.  The prefill kernel keeps MFMA accumulators in VGPRs (its
+# softmax reads every accumulator with VALU instructions; AGPR-form accumulators cost a
+# copy per element per block).
+EXTRA_FLAGS = {"fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -38,7 +42,7 @@ def hipcc():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON_FLAGS
+    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON_FLAGS + EXTRA_FLAGS.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in line)

@@ -32,6 +32,16 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4): lane i of the
+// wave writes lds_wave_base + 16 * i; lds_wave_base must be the same for the whole wave.
+// The builtin only exists for the device pass; keeping it out of the host pass keeps
+// clang emitting the host launch stubs of the kernels that use it.
+__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+#endif
+}
+
 // sin and cos of 2*pi*rev for |rev| <= 0.5 (hardware v_sin/v_cos take revolutions).
 __device__ __forceinline__ void sincos_rev(float rev, float* s, float* c) {
   *s = __builtin_amdgcn_sinf(rev);

@@ -17,23 +17,29 @@
 //    held in registers for the whole kernel.  In the accumulator layout a lane owns
 //    one query column, so the row max and row sum are in-lane except for one swap
 //    with the lane 32 apart.
+//  * The running max is subtracted inside the matrix product: one extra k-step pairs
+//    a constant 1 on the K side with -m on the Q side, so the accumulators already
+//    hold s - m and each probability is a single exp2.  m is kept bf16-exact for
+//    that purpose; it is only a reference point, so any value works as long as the
+//    same one scales o, l and the final lse.
+//  * The reference m is raised only when a block's max exceeds it by more than 8
+//    (in log2 units); p is then at most 2^8, which fp32 accumulators and bf16 P carry
+//    without loss, and o / l is unchanged because both use the same reference.
 //  * O^T = V^T P^T: P^T is the B operand exactly as the S^T accumulators sit in
 //    registers (the contraction order over keys is permuted to match), V^T is read
-//    from a row-major LDS tile with ds_read_b64_tr_b16.  Again a lane owns one query,
-//    so the rescale factor is a per-lane scalar.
+//    from a row-major LDS tile with ds_read_b64_tr_b16.  A lane owns one query, so
+//    the rescale factor is a per-lane scalar.
 //  * Logits are in the base-2 domain: RoPE'd q is pre-multiplied by log2(e)/sqrt(d_h)
 //    before rounding to bf16, so p = exp2(s - m).
-//  * The running max is raised only when a block's max exceeds it by more than 8
-//    (in log2 units).  p is then at most 2^8, which fp32 accumulators and bf16 P
-//    carry without loss, and the final o / l is unchanged because o and l are
-//    scaled by the same reference; the rescale is skipped in most blocks.
-//  * RoPE: q rotated once at load; K rotated when a block is copied from HBM to LDS,
-//    using per-thread fixed angle offsets combined with a per-block base angle
-//    (angle addition), all angles reduced modulo one turn in fp64.
-//  * K/V blocks are double-buffered in LDS; the next block's global loads are in
-//    flight while the current one is consumed.  Work is ordered longest-first for
-//    causal load balance and mapped so all query blocks of one KV head land on one
-//    XCD (shared L2).
+//  * K and V move from HBM to LDS with direct 16-byte loads (global_load_lds_dwordx4),
+//    so no registers are tied up by loads in flight.  V lands in its final, xor-swizzled
+//    layout; K lands in a staging area and each thread rotates the chunks it loaded
+//    (RoPE at load) into the padded K tile.  The rotation angles advance from block
+//    to block by angle addition and are re-derived exactly (fp64 reduction) every 16
+//    blocks.
+//  * K/V blocks are double-buffered; the next block's loads are in flight while the
+//    current one is consumed.  Work is ordered longest-first for causal load balance
+//    and mapped so all query blocks of one KV head land on one XCD (shared L2).
 #include <math.h>
 
 #include "attn_common.h"
@@ -48,28 +54,53 @@ constexpr int kNW = 4;        // waves per workgroup
 constexpr int kQW = 64;       // query rows per wave
 constexpr int kBN = 64;       // keys per block
 constexpr int kThreads = kNW * kWave;
+constexpr int kResync = 16;   // blocks between exact re-derivations of the RoPE angles
 
 template <int D>
 struct Cfg {
-  static constexpr int KS = D / 16;             // k-steps of the QK^T product
-  static constexpr int DB = D / 32;             // 32-wide dim blocks of the output
-  static constexpr int KSTR = D + 8;            // K row stride in LDS (bf16)
-  static constexpr int VSTR = D + 32;           // V row stride in LDS (bf16)
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int KS = D / 16;                 // k-steps of the QK^T product
+  static constexpr int DB = D / 32;                 // 32-wide dim blocks of the output
+  static constexpr int KSTR = D + 8;                // rotated-K row stride in LDS (bf16)
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int NCH = kBN * CPR / kThreads;  // chunks per thread per tensor
-  static constexpr int KROW_STEP = kThreads / CPR;  // key stride between a thread's chunks
+  static constexpr int RSTEP = kWave / CPR;         // rows between a thread's chunks
 };
 
-__device__ __forceinline__ void lds_barrier() { __syncthreads(); }
+// xor swizzle of the 16-byte chunk index of V row r: the transpose reads of a half
+// wave (4 rows x 64 bytes) then touch 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3);
+  else return 4 * ((r >> 1) & 1);
+}
+
+__device__ __forceinline__ void cmul(float& c, float& s, float sc, float ss) {
+  const float nc = c * sc - s * ss;
+  const float ns = c * ss + s * sc;
+  c = nc;
+  s = ns;
+}
+
+// Round up to a bf16-representable value (finite x).
+__device__ __forceinline__ float bf16_ceil(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  uint32_t r = u & 0xffff0000u;
+  const float t = __builtin_bit_cast(float, r);
+  if (t < x) r = (x > 0.f) ? r + 0x10000u : r - 0x10000u;
+  return __builtin_bit_cast(float, r);
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 }  // namespace
 
-template <int D, int HP>
+template <int D, int HP, bool ROPE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][kBN * C::KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][kBN * C::VSTR];
+  __shared__ __attribute__((aligned(16))) u32x4 Vs[2][kBN * C::CPR];
+  __shared__ __attribute__((aligned(16))) u32x4 Kraw[kBN * C::CPR];
 
   const int tid = threadIdx.x;
   const int wid = tid / kWave;
@@ -129,7 +160,7 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float x0 = bf16_lo(raw[e]), x1 = bf16_hi(raw[e]);
-          if (p.use_rope) {
+          if constexpr (ROPE) {
             const float tr = rope_turns(pos + t, p.rope_c[ks * 8 + g * 4 + e]);
             float sn, cs;
             sincos_rev(tr, &sn, &cs);
@@ -143,69 +174,76 @@ void fwd_bf16_kernel(FwdParams p) {
       }
     }
   }
+  // Extra k-step: K side holds 1 in slot 0 of the g = 0 lanes, Q side holds -m there.
+  const bf16x8 ones_op = __builtin_bit_cast(bf16x8, (u32x4){g == 0 ? 0x3f80u : 0u, 0u, 0u, 0u});
 
-  // ---- per-thread K/V copy assignment and fixed RoPE offsets.
-  const int crow = tid / C::CPR;        // first key row of this thread's chunks
-  const int cchk = tid % C::CPR;        // 16-byte chunk (8 dims = 4 pairs) within the row
-  float off_c[C::NCH][4], off_s[C::NCH][4];
-  double base_c[4];
-  if (p.use_rope) {
+  // ---- this thread's share of the K/V block copies: chunk `slot` of rows row0 + j*RSTEP.
+  const int slot = lane % C::CPR;
+  const int row0 = wid * C::NCH * C::RSTEP + lane / C::CPR;
+
+  // RoPE angle state for the 4 pairs of this thread's chunk: (cos, sin) at key
+  // tile*64 + row0, plus the per-row and per-block steps.
+  float ac[4], as[4], rc[4], rs[4], tc[4], ts[4];
+  double cturn[4];
+  if constexpr (ROPE) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) base_c[e] = p.rope_c[cchk * 4 + e];
-#pragma unroll
-    for (int i = 0; i < C::NCH; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float tr = rope_turns((int64_t)(crow + i * C::KROW_STEP), base_c[e]);
-        sincos_rev(tr, &off_s[i][e], &off_c[i][e]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      cturn[e] = p.rope_c[slot * 4 + e];
+      sincos_rev(rope_turns((int64_t)C::RSTEP, cturn[e]), &rs[e], &rc[e]);
+      sincos_rev(rope_turns((int64_t)kBN, cturn[e]), &ts[e], &tc[e]);
+    }
   }
 
-  u32x4 kreg[C::NCH], vreg[C::NCH];
-  auto load_tile = [&](int tile) {
+  auto issue_loads = [&](int tile, int vbuf) {
     const int k0 = tile * kBN;
 #pragma unroll
-    for (int i = 0; i < C::NCH; ++i) {
-      const int s = k0 + crow + i * C::KROW_STEP;
-      if (s < S) {
-        kreg[i] = *(const u32x4*)(kg + (size_t)s * D + cchk * 8);
-        vreg[i] = *(const u32x4*)(vg + (size_t)s * D + cchk * 8);
-      } else {
-        kreg[i] = (u32x4){0u, 0u, 0u, 0u};
-        vreg[i] = (u32x4){0u, 0u, 0u, 0u};
-      }
+    for (int j = 0; j < C::NCH; ++j) {
+      const int r = row0 + j * C::RSTEP;
+      const int s = min(k0 + r, S - 1);  // rows past S are never visible; any finite data will do
+      const int wbase = (wid * C::NCH + j) * kWave;
+      load_lds16(kg + (size_t)s * D + slot * 8, &Kraw[wbase]);
+      load_lds16(vg + (size_t)s * D + (slot ^ vswz<D>(r)) * 8, &Vs[vbuf][wbase]);
     }
   };
-  auto store_tile = [&](int tile, int buf) {
-    if (p.use_rope) {
-      const int64_t k0 = (int64_t)tile * kBN;
-      float bc[4], bs[4];
+  // Rotate this thread's raw K chunks of block `tile` into Ks[kbuf].
+  auto rotate_k = [&](int tile, int kbuf) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's direct loads have landed
+    if constexpr (ROPE) {
+      if (tile % kResync == 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sincos_rev(rope_turns(k0, base_c[e]), &bs[e], &bc[e]);
+        for (int e = 0; e < 4; ++e)
+          sincos_rev(rope_turns((int64_t)tile * kBN + row0, cturn[e]), &as[e], &ac[e]);
+      }
+      float c[4], s[4];
 #pragma unroll
-      for (int i = 0; i < C::NCH; ++i) {
+      for (int e = 0; e < 4; ++e) {
+        c[e] = ac[e];
+        s[e] = as[e];
+      }
+#pragma unroll
+      for (int j = 0; j < C::NCH; ++j) {
+        const u32x4 raw = Kraw[(wid * C::NCH + j) * kWave + lane];
         u32x4 out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float c = bc[e] * off_c[i][e] - bs[e] * off_s[i][e];
-          const float s = bs[e] * off_c[i][e] + bc[e] * off_s[i][e];
-          const float x0 = bf16_lo(kreg[i][e]), x1 = bf16_hi(kreg[i][e]);
-          out[e] = pack_bf16(x0 * c - x1 * s, x0 * s + x1 * c);
+          const float x0 = bf16_lo(raw[e]), x1 = bf16_hi(raw[e]);
+          out[e] = pack_bf16(x0 * c[e] - x1 * s[e], x0 * s[e] + x1 * c[e]);
+          if (j + 1 < C::NCH) cmul(c[e], s[e], rc[e], rs[e]);
         }
-        *(u32x4*)&Ks[buf][(crow + i * C::KROW_STEP) * C::KSTR + cchk * 8] = out;
+        *(u32x4*)&Ks[kbuf][(row0 + j * C::RSTEP) * C::KSTR + slot * 8] = out;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cmul(ac[e], as[e], tc[e], ts[e]);
     } else {
 #pragma unroll
-      for (int i = 0; i < C::NCH; ++i)
-        *(u32x4*)&Ks[buf][(crow + i * C::KROW_STEP) * C::KSTR + cchk * 8] = kreg[i];
+      for (int j = 0; j < C::NCH; ++j)
+        *(u32x4*)&Ks[kbuf][(row0 + j * C::RSTEP) * C::KSTR + slot * 8] =
+            Kraw[(wid * C::NCH + j) * kWave + lane];
     }
-#pragma unroll
-    for (int i = 0; i < C::NCH; ++i)
-      *(u32x4*)&Vs[buf][(crow + i * C::KROW_STEP) * C::VSTR + cchk * 8] = vreg[i];
   };
 
   // ---- running state: two query n-blocks per lane.
-  float m_run[2] = {-INFINITY, -INFINITY};
+  float m_ref[2] = {-INFINITY, -INFINITY};  // bf16-exact reference max (base 2)
   float l_run[2] = {0.f, 0.f};
   f32x16 o[C::DB][2];
 #pragma unroll
@@ -216,27 +254,33 @@ void fwd_bf16_kernel(FwdParams p) {
       for (int r = 0; r < 16; ++r) o[db][nb][r] = 0.f;
 
   if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0, 0);
+    issue_loads(0, 0);
+    rotate_k(0, 0);
   }
   for (int it = 0; it < n_tiles; ++it) {
     const int buf = it & 1;
     const bool more = it + 1 < n_tiles;
-    if (more) load_tile(it + 1);
-    lds_barrier();
+    __syncthreads();  // block `it` is in LDS; everyone is done with block it-1
+    if (more) issue_loads(it + 1, buf ^ 1);
 
     const int k0 = it * kBN;
     if (k0 < nk_wave) {
       const __bf16* kb = &Ks[buf][0];
-      const __bf16* vb = &Vs[buf][0];
-      // S^T = K Q^T
+      const char* vb = (const char*)&Vs[buf][0];
+      // S'^T = K Q^T - m (extra k-step), per query column
       f32x16 s[2][2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < 2; ++nb) {
+          const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
+          const bf16x8 bop = __builtin_bit_cast(
+              bf16x8, (u32x4){g == 0 ? (__builtin_bit_cast(uint32_t, -bias) >> 16) : 0u, 0u, 0u, 0u});
+          f32x16 acc;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[mb][nb][r] = 0.f;
+          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+          s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_op, bop, acc, 0, 0, 0);
+        }
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
@@ -252,13 +296,13 @@ void fwd_bf16_kernel(FwdParams p) {
       if (need_mask) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          const int64_t qp = pos + wrow0 + nb * 32 + l32;
+          const int64_t lim = pos + wrow0 + nb * 32 + l32;  // last visible key of this query
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = k0 + mb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-              const bool vis = key < S && (!p.causal || (int64_t)key <= qp);
+              const bool vis = key < S && (!p.causal || (int64_t)key <= lim);
               if (!vis) s[mb][nb][r] = -INFINITY;
             }
         }
@@ -267,26 +311,37 @@ void fwd_bf16_kernel(FwdParams p) {
       bf16x8 pop[2][4];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        float tmax = -INFINITY;
+        float t0 = max3(s[0][nb][0], s[0][nb][1], s[0][nb][2]);
+        float t1 = max3(s[1][nb][0], s[1][nb][1], s[1][nb][2]);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][nb][r]);
+        for (int r = 3; r < 15; r += 2) {
+          t0 = max3(t0, s[0][nb][r], s[0][nb][r + 1]);
+          t1 = max3(t1, s[1][nb][r], s[1][nb][r + 1]);
+        }
+        float tmax = max3(t0, s[0][nb][15], fmaxf(t1, s[1][nb][15]));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const bool need = tmax > m_run[nb] + 8.f;
+        // tmax is relative to the bias the product subtracted
+        const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
+        const float tabs = tmax + bias;
+        const bool need = tabs > m_ref[nb] + 8.f;
+        float delta = 0.f;
         if (__any(need)) {
-          // lanes that keep their reference use alpha = 1 (their m may still be -inf)
-          const float m_new = need ? tmax : m_run[nb];
-          const float alpha = need ? fast_exp2(m_run[nb] - m_new) : 1.f;  // 0 when m_run was -inf
+          __asm__ volatile("");  // keep this rare path a real branch (no speculation)
+          const float m_new = need ? bf16_ceil(tabs) : m_ref[nb];
+          const float alpha = need ? fast_exp2(m_ref[nb] - m_new) : 1.f;  // 0 when m_ref was -inf
+          delta = need ? m_new - bias : 0.f;
           l_run[nb] *= alpha;
 #pragma unroll
           for (int db = 0; db < C::DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[db][nb][r] *= alpha;
-          m_run[nb] = m_new;
+          m_ref[nb] = m_new;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[mb][nb][r] -= delta;
         }
-        const float mu = (m_run[nb] == -INFINITY) ? 0.f : m_run[nb];
-        float psum = 0.f;
+        float lsum = l_run[nb];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -294,30 +349,31 @@ void fwd_bf16_kernel(FwdParams p) {
             u32x4 pk;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float p0 = fast_exp2(s[mb][nb][8 * h + 2 * e] - mu);
-              const float p1 = fast_exp2(s[mb][nb][8 * h + 2 * e + 1] - mu);
-              psum += p0 + p1;
+              const float p0 = fast_exp2(s[mb][nb][8 * h + 2 * e]);
+              const float p1 = fast_exp2(s[mb][nb][8 * h + 2 * e + 1]);
               pk[e] = pack_bf16(p0, p1);
+              lsum += p0 + p1;
             }
             pop[nb][mb * 2 + h] = __builtin_bit_cast(bf16x8, pk);
           }
-        l_run[nb] += psum;
+        l_run[nb] = lsum;
       }
       // O^T += V^T P^T
       const int a16 = lane / 16, lam = lane % 16;
-      const int trow = 4 * g + lam / 4;
-      const int tcol = 16 * (a16 % 2) + 4 * (lam % 4);
 #pragma unroll
       for (int kstep = 0; kstep < 4; ++kstep) {
-        const int kwin = kstep * 16;
+        const int r1 = kstep * 16 + 4 * g + lam / 4;  // rows for the two transpose reads
+        const int r2 = r1 + 8;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const __bf16* a0p = vb + (kwin + trow) * C::VSTR + db * 32 + tcol;
-          const __bf16* a1p = a0p + 8 * C::VSTR;
+          const int col = db * 32 + 16 * (a16 % 2) + 4 * (lam % 4);   // first of 4 dims
+          const int c = col / 8, half = (col % 8) / 4;
+          const int off1 = (r1 * C::CPR + (c ^ vswz<D>(r1))) * 16 + half * 8;
+          const int off2 = (r2 * C::CPR + (c ^ vswz<D>(r2))) * 16 + half * 8;
           const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(a0p));
+              (__attribute__((address_space(3))) s16x4*)(vb + off1));
           const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(a1p));
+              (__attribute__((address_space(3))) s16x4*)(vb + off2));
           const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
           const bf16x8 a = __builtin_bit_cast(bf16x8, (u32x4){w0[0], w0[1], w1[0], w1[1]});
 #pragma unroll
@@ -326,7 +382,7 @@ void fwd_bf16_kernel(FwdParams p) {
         }
       }
     }
-    if (more) store_tile(it + 1, buf ^ 1);
+    if (more) rotate_k(it + 1, buf ^ 1);
   }
 
   // ---- epilogue: O = o / l, lse = (m + log2 l) ln 2.
@@ -348,13 +404,13 @@ void fwd_bf16_kernel(FwdParams p) {
         }
       if (p.lse && g == 0)
         p.lse[((size_t)b * p.Hq + hq) * (size_t)T + t] =
-            lt > 0.f ? (m_run[nb] + __log2f(lt)) * kLn2 : -INFINITY;
+            lt > 0.f ? (m_ref[nb] + __log2f(lt)) * kLn2 : -INFINITY;
     }
   }
 }
 
 namespace {
-template <int D, int HP>
+template <int D, int HP, bool ROPE>
 hipError_t launch_one(FwdParams q, hipStream_t stream) {
   constexpr int RH = kNW * kQW / HP;
   q.n_qblocks = (q.T + RH - 1) / RH;
@@ -362,16 +418,21 @@ hipError_t launch_one(FwdParams q, hipStream_t stream) {
   q.xcd_remap = (q.n_groups % 8) == 0;
   const long long grid = (long long)q.n_qblocks * q.n_groups;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, HP>), dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, HP, ROPE>), dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
   return hipGetLastError();
+}
+
+template <int D, int HP>
+hipError_t launch_r(const FwdParams& p, hipStream_t stream) {
+  return p.use_rope ? launch_one<D, HP, true>(p, stream) : launch_one<D, HP, false>(p, stream);
 }
 
 template <int D>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
-  if (G % 4 == 0) return launch_one<D, 4>(p, stream);
-  if (G % 2 == 0) return launch_one<D, 2>(p, stream);
-  return launch_one<D, 1>(p, stream);
+  if (G % 4 == 0) return launch_r<D, 4>(p, stream);
+  if (G % 2 == 0) return launch_r<D, 2>(p, stream);
+  return launch_r<D, 1>(p, stream);
 }
 }  // namespace
 
