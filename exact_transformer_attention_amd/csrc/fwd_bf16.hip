@@ -42,6 +42,8 @@
 //    and mapped so all query blocks of one KV head land on one XCD (shared L2).
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_common.h"
 #include "fwd_params.h"
 #include "launchers.h"
@@ -50,8 +52,9 @@ namespace attn {
 
 namespace {
 
-constexpr int kNW = 4;        // waves per workgroup
-constexpr int kQW = 64;       // query rows per wave
+constexpr int kNB = 1;        // 32-query n-blocks per wave
+constexpr int kNW = 8;        // waves per workgroup (two per SIMD)
+constexpr int kQW = 32 * kNB; // query rows per wave
 constexpr int kBN = 64;       // keys per block
 constexpr int kThreads = kNW * kWave;
 constexpr int kResync = 16;   // blocks between exact re-derivations of the RoPE angles
@@ -95,12 +98,12 @@ __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(
 }  // namespace
 
 template <int D, int HP, bool ROPE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kNW / 4, kNW / 4)))
 void fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][kBN * C::KSTR];
-  __shared__ __attribute__((aligned(16))) u32x4 Vs[2][kBN * C::CPR];
-  __shared__ __attribute__((aligned(16))) u32x4 Kraw[kBN * C::CPR];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][kBN * C::KSTR];   // rotated K, padded rows
+  __shared__ __attribute__((aligned(16))) u32x4 Vs[2][kBN * C::CPR];     // V, swizzled 16-byte chunks
+  __shared__ __attribute__((aligned(16))) u32x4 Kraw[2][kBN * C::CPR];   // K as loaded
 
   const int tid = threadIdx.x;
   const int wid = tid / kWave;
@@ -145,11 +148,11 @@ void fwd_bf16_kernel(FwdParams p) {
   const int n_tiles = (nk_wg + kBN - 1) / kBN;
 
   // ---- Q^T operand in registers: lane holds query l32 of n-block nb, dims ks*16 + g*8.
-  bf16x8 qop[2][C::KS];
+  bf16x8 qop[kNB][C::KS];
   {
     const float qscale = kLog2e / sqrtf((float)D);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < kNB; ++nb) {
       const int t = wrow0 + nb * 32 + l32;
       const bool ok = t < T;
 #pragma unroll
@@ -194,26 +197,30 @@ void fwd_bf16_kernel(FwdParams p) {
     }
   }
 
-  auto issue_loads = [&](int tile, int vbuf) {
+  // Direct-to-LDS loads: raw K of block `tile` into Kraw[tile & 1] (two blocks ahead of
+  // its use), V of block `tile` into Vs[tile & 1] (one block ahead).  NCH loads each.
+  auto load_k = [&](int tile) {
+    const int k0 = tile * kBN;
+#pragma unroll
+    for (int j = 0; j < C::NCH; ++j) {
+      const int s = min(k0 + row0 + j * C::RSTEP, S - 1);  // rows past S are never visible
+      load_lds16(kg + (size_t)s * D + slot * 8, &Kraw[tile & 1][(wid * C::NCH + j) * kWave]);
+    }
+  };
+  auto load_v = [&](int tile) {
     const int k0 = tile * kBN;
 #pragma unroll
     for (int j = 0; j < C::NCH; ++j) {
       const int r = row0 + j * C::RSTEP;
-      const int s = min(k0 + r, S - 1);  // rows past S are never visible; any finite data will do
-      const int wbase = (wid * C::NCH + j) * kWave;
-      load_lds16(kg + (size_t)s * D + slot * 8, &Kraw[wbase]);
-      load_lds16(vg + (size_t)s * D + (slot ^ vswz<D>(r)) * 8, &Vs[vbuf][wbase]);
+      const int s = min(k0 + r, S - 1);
+      load_lds16(vg + (size_t)s * D + (slot ^ vswz<D>(r)) * 8, &Vs[tile & 1][(wid * C::NCH + j) * kWave]);
     }
   };
-  // Rotate this thread's raw K chunks of block `tile` into Ks[kbuf].
-  auto rotate_k = [&](int tile, int kbuf) {
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's direct loads have landed
+  // Rotate this thread's raw K chunks of block `tile` into Ks[tile & 1].  The caller has
+  // waited for the loads of that block.
+  auto rotate_k = [&](int tile, auto kbc) {
+    constexpr int kb = decltype(kbc)::value;  // == tile & 1
     if constexpr (ROPE) {
-      if (tile % kResync == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sincos_rev(rope_turns((int64_t)tile * kBN + row0, cturn[e]), &as[e], &ac[e]);
-      }
       float c[4], s[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -222,7 +229,7 @@ void fwd_bf16_kernel(FwdParams p) {
       }
 #pragma unroll
       for (int j = 0; j < C::NCH; ++j) {
-        const u32x4 raw = Kraw[(wid * C::NCH + j) * kWave + lane];
+        const u32x4 raw = Kraw[kb][(wid * C::NCH + j) * kWave + lane];
         u32x4 out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -230,72 +237,136 @@ void fwd_bf16_kernel(FwdParams p) {
           out[e] = pack_bf16(x0 * c[e] - x1 * s[e], x0 * s[e] + x1 * c[e]);
           if (j + 1 < C::NCH) cmul(c[e], s[e], rc[e], rs[e]);
         }
-        *(u32x4*)&Ks[kbuf][(row0 + j * C::RSTEP) * C::KSTR + slot * 8] = out;
+        *(u32x4*)&Ks[kb][(row0 + j * C::RSTEP) * C::KSTR + slot * 8] = out;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) cmul(ac[e], as[e], tc[e], ts[e]);
     } else {
 #pragma unroll
       for (int j = 0; j < C::NCH; ++j)
-        *(u32x4*)&Ks[kbuf][(row0 + j * C::RSTEP) * C::KSTR + slot * 8] =
-            Kraw[(wid * C::NCH + j) * kWave + lane];
+        *(u32x4*)&Ks[kb][(row0 + j * C::RSTEP) * C::KSTR + slot * 8] =
+            Kraw[kb][(wid * C::NCH + j) * kWave + lane];
     }
   };
+  // Exact angles of this thread's first key of block `tile` (every kResync blocks; the
+  // angle addition in rotate_k advances them in between).
+  auto resync = [&](int tile) {
+    if constexpr (ROPE) {
+      if (tile % kResync == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sincos_rev(rope_turns((int64_t)tile * kBN + row0, cturn[e]), &as[e], &ac[e]);
+      }
+    }
+  };
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0f70); };  // vmcnt(0)
 
   // ---- running state: two query n-blocks per lane.
-  float m_ref[2] = {-INFINITY, -INFINITY};  // bf16-exact reference max (base 2)
-  float l_run[2] = {0.f, 0.f};
-  f32x16 o[C::DB][2];
+  float m_ref[kNB], l_run[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    m_ref[nb] = -INFINITY;  // bf16-exact reference max (base 2)
+    l_run[nb] = 0.f;
+  }
+  f32x16 o[C::DB][kNB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][nb][r] = 0.f;
 
-  if (n_tiles > 0) {
-    issue_loads(0, 0);
-    rotate_k(0, 0);
-  }
-  for (int it = 0; it < n_tiles; ++it) {
-    const int buf = it & 1;
-    const bool more = it + 1 < n_tiles;
-    __syncthreads();  // block `it` is in LDS; everyone is done with block it-1
-    if (more) issue_loads(it + 1, buf ^ 1);
-
-    const int k0 = it * kBN;
-    if (k0 < nk_wave) {
-      const __bf16* kb = &Ks[buf][0];
-      const char* vb = (const char*)&Vs[buf][0];
-      // S'^T = K Q^T - m (extra k-step), per query column
-      f32x16 s[2][2];
+  // S'^T = K Q^T - m for both 32-key halves and both query n-blocks.
+  auto qk = [&](const __bf16* kb, f32x16 (&s)[2][kNB]) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-          const bf16x8 bop = __builtin_bit_cast(
-              bf16x8, (u32x4){g == 0 ? (__builtin_bit_cast(uint32_t, -bias) >> 16) : 0u, 0u, 0u, 0u});
-          f32x16 acc;
+      for (int nb = 0; nb < kNB; ++nb) {
+        const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
+        const bf16x8 bop = __builtin_bit_cast(
+            bf16x8, (u32x4){g == 0 ? (__builtin_bit_cast(uint32_t, -bias) >> 16) : 0u, 0u, 0u, 0u});
+        f32x16 acc;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-          s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_op, bop, acc, 0, 0, 0);
-        }
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 a = *(const bf16x8*)(kb + (mb * 32 + l32) * C::KSTR + ks * 16 + g * 8);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[nb][ks], s[mb][nb], 0, 0, 0);
-        }
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_op, bop, acc, 0, 0, 0);
       }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 a = *(const bf16x8*)(kb + (mb * 32 + l32) * C::KSTR + ks * 16 + g * 8);
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+          s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[nb][ks], s[mb][nb], 0, 0, 0);
+      }
+    }
+  };
+  // exp2 of one 32-key half for both n-blocks -> bf16 P operands, row sums.
+  auto expo = [&](f32x16 (&s)[2][kNB], int mb, bf16x8 (&pop)[kNB][4]) {
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      float lsum = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(s[mb][nb][8 * h + 2 * e]);
+          const float p1 = fast_exp2(s[mb][nb][8 * h + 2 * e + 1]);
+          pk[e] = pack_bf16(p0, p1);
+          lsum += p0 + p1;
+        }
+        pop[nb][mb * 2 + h] = __builtin_bit_cast(bf16x8, pk);
+      }
+      l_run[nb] += lsum;
+    }
+  };
+  const int a16 = lane / 16, lam = lane % 16;
+  // O^T += V^T P^T for one 16-key step.
+  auto pv = [&](const char* vb, int kstep, const bf16x8 (&pop)[kNB][4]) {
+    const int r1 = kstep * 16 + 4 * g + lam / 4;  // rows of the two transpose reads
+    const int r2 = r1 + 8;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int col = db * 32 + 16 * (a16 % 2) + 4 * (lam % 4);  // first of 4 dims
+      const int c = col / 8, half = (col % 8) / 4;
+      const int off1 = (r1 * C::CPR + (c ^ vswz<D>(r1))) * 16 + half * 8;
+      const int off2 = (r2 * C::CPR + (c ^ vswz<D>(r2))) * 16 + half * 8;
+      const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vb + off1));
+      const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vb + off2));
+      const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, (u32x4){w0[0], w0[1], w1[0], w1[1]});
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+        o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[nb][kstep], o[db][nb], 0, 0, 0);
+    }
+  };
+
+  // ---- one block of keys.  PAR = it & 1 is a compile-time constant so that the LDS
+  // buffers read (Ks[PAR], Vs[PAR]) and written (Ks[PAR ^ 1], Kraw[PAR], Vs[PAR ^ 1]) are
+  // provably distinct and the scheduler may interleave the rotation of block it+1 with
+  // the products of block it.
+  auto step = [&](auto par, int it) {
+    constexpr int PAR = decltype(par)::value;
+    __syncthreads();  // block it is rotated and landed; everyone is done with block it-1
+    if (it + 2 < n_tiles) load_k(it + 2);
+    if (it + 1 < n_tiles) load_v(it + 1);
+    const bool rot = it + 1 < n_tiles;  // rotate block it+1 during this iteration
+    if (rot) resync(it + 1);
+    const int k0 = it * kBN;
+    const __bf16* kbuf = &Ks[PAR][0];
+    const char* vbuf = (const char*)&Vs[PAR][0];
+    if (k0 < nk_wave) {
+      f32x16 s[2][kNB];
+      qk(kbuf, s);
+      if (rot) rotate_k(it + 1, std::integral_constant<int, PAR ^ 1>{});
       // mask (diagonal / tail blocks only)
       const bool need_mask = (k0 + kBN > S) || (p.causal && (int64_t)(k0 + kBN - 1) > pos + wrow0);
       if (need_mask) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < kNB; ++nb) {
           const int64_t lim = pos + wrow0 + nb * 32 + l32;  // last visible key of this query
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
@@ -307,10 +378,13 @@ void fwd_bf16_kernel(FwdParams p) {
             }
         }
       }
-      // online softmax
-      bf16x8 pop[2][4];
+      // block max (relative to the reference the product subtracted); raise the
+      // reference only when it is exceeded by more than 8
+      bool need[kNB];
+      float tabs[kNB];
+      bool any_need = false;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < kNB; ++nb) {
         float t0 = max3(s[0][nb][0], s[0][nb][1], s[0][nb][2]);
         float t1 = max3(s[1][nb][0], s[1][nb][1], s[1][nb][2]);
 #pragma unroll
@@ -320,16 +394,19 @@ void fwd_bf16_kernel(FwdParams p) {
         }
         float tmax = max3(t0, s[0][nb][15], fmaxf(t1, s[1][nb][15]));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        // tmax is relative to the bias the product subtracted
         const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-        const float tabs = tmax + bias;
-        const bool need = tabs > m_ref[nb] + 8.f;
-        float delta = 0.f;
-        if (__any(need)) {
-          __asm__ volatile("");  // keep this rare path a real branch (no speculation)
-          const float m_new = need ? bf16_ceil(tabs) : m_ref[nb];
-          const float alpha = need ? fast_exp2(m_ref[nb] - m_new) : 1.f;  // 0 when m_ref was -inf
-          delta = need ? m_new - bias : 0.f;
+        tabs[nb] = tmax + bias;
+        need[nb] = tabs[nb] > m_ref[nb] + 8.f;
+        any_need |= need[nb];
+      }
+      if (__any(any_need)) {
+        __asm__ volatile("");  // keep this rare path a real branch (no speculation)
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
+          const float m_new = need[nb] ? bf16_ceil(tabs[nb]) : m_ref[nb];
+          const float alpha = need[nb] ? fast_exp2(m_ref[nb] - m_new) : 1.f;  // 0 when m_ref was -inf
+          const float delta = need[nb] ? m_new - bias : 0.f;
           l_run[nb] *= alpha;
 #pragma unroll
           for (int db = 0; db < C::DB; ++db)
@@ -341,53 +418,39 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[mb][nb][r] -= delta;
         }
-        float lsum = l_run[nb];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            u32x4 pk;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p0 = fast_exp2(s[mb][nb][8 * h + 2 * e]);
-              const float p1 = fast_exp2(s[mb][nb][8 * h + 2 * e + 1]);
-              pk[e] = pack_bf16(p0, p1);
-              lsum += p0 + p1;
-            }
-            pop[nb][mb * 2 + h] = __builtin_bit_cast(bf16x8, pk);
-          }
-        l_run[nb] = lsum;
       }
-      // O^T += V^T P^T
-      const int a16 = lane / 16, lam = lane % 16;
-#pragma unroll
-      for (int kstep = 0; kstep < 4; ++kstep) {
-        const int r1 = kstep * 16 + 4 * g + lam / 4;  // rows for the two transpose reads
-        const int r2 = r1 + 8;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const int col = db * 32 + 16 * (a16 % 2) + 4 * (lam % 4);   // first of 4 dims
-          const int c = col / 8, half = (col % 8) / 4;
-          const int off1 = (r1 * C::CPR + (c ^ vswz<D>(r1))) * 16 + half * 8;
-          const int off2 = (r2 * C::CPR + (c ^ vswz<D>(r2))) * 16 + half * 8;
-          const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vb + off1));
-          const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vb + off2));
-          const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, (u32x4){w0[0], w0[1], w1[0], w1[1]});
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[nb][kstep], o[db][nb], 0, 0, 0);
-        }
-      }
+      // probabilities and O^T += V^T P^T; the exponentials of the second key half run
+      // under the products of the first
+      bf16x8 pop[kNB][4];
+      expo(s, 0, pop);
+      pv(vbuf, 0, pop);
+      pv(vbuf, 1, pop);
+      expo(s, 1, pop);
+      pv(vbuf, 2, pop);
+      pv(vbuf, 3, pop);
+    } else if (rot) {
+      rotate_k(it + 1, std::integral_constant<int, PAR ^ 1>{});
     }
-    if (more) rotate_k(it + 1, buf ^ 1);
+    wait_loads();  // this thread's loads issued above have landed before the next barrier
+  };
+
+  // ---- prologue: raw K of blocks 0 and 1 and V of block 0 in flight; block 0 rotated.
+  if (n_tiles > 0) {
+    load_k(0);
+    load_v(0);
+    if (n_tiles > 1) load_k(1);
+    wait_loads();
+    resync(0);
+    rotate_k(0, std::integral_constant<int, 0>{});
+  }
+  for (int it = 0; it < n_tiles; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
   // ---- epilogue: O = o / l, lse = (m + log2 l) ln 2.
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < kNB; ++nb) {
     const float lt = l_run[nb] + __shfl_xor(l_run[nb], 32);
     const int t = wrow0 + nb * 32 + l32;
     if (t < T) {
