@@ -9,37 +9,40 @@
 // masking) and key blocks hidden from a whole wave are skipped.
 //
 // Mapping onto CDNA4 (wave64, v_mfma_f32_32x32x16_bf16):
-//  * workgroup = 4 waves; each wave owns 64 query rows of one head.  The heads that
-//    share one KV head (grouped-query attention) are packed into the same workgroup
-//    (HP heads per workgroup), so every K/V block loaded, and rotated, once serves
-//    256 query rows.
+//  * workgroup = 8 waves, two per SIMD; each wave owns 32 query rows of one head.  The
+//    heads that share one KV head (grouped-query attention) are packed into the same
+//    workgroup (HP heads per workgroup), so every K/V block loaded, and rotated, once
+//    serves 256 query rows.  With one 32-query block per wave the per-wave state fits
+//    in VGPRs, and the two waves of a SIMD overlap one's softmax/RoPE work with the
+//    other's matrix products.
 //  * S^T = K Q^T: K (64-key block) is the A operand read from LDS, Q^T the B operand
 //    held in registers for the whole kernel.  In the accumulator layout a lane owns
-//    one query column, so the row max and row sum are in-lane except for one swap
-//    with the lane 32 apart.
+//    one query column, so row sums are in-lane except for one swap with the lane 32
+//    apart.
 //  * The running max is subtracted inside the matrix product: one extra k-step pairs
 //    a constant 1 on the K side with -m on the Q side, so the accumulators already
-//    hold s - m and each probability is a single exp2.  m is kept bf16-exact for
-//    that purpose; it is only a reference point, so any value works as long as the
-//    same one scales o, l and the final lse.
-//  * The reference m is raised only when a block's max exceeds it by more than 8
-//    (in log2 units); p is then at most 2^8, which fp32 accumulators and bf16 P carry
-//    without loss, and o / l is unchanged because both use the same reference.
+//    hold s - m and each probability is a single exp2.  m is kept bf16-exact for that
+//    purpose; it is only a reference point, so any value works as long as the same one
+//    scales o, l and the final lse.
+//  * The reference is not recomputed every block.  Probabilities are formed against the
+//    current reference; only when a row has no reference yet, or a half block's row sum
+//    exceeds 2^16 (the reference is stale by more than ~16 in log2 units), is the exact
+//    block max taken, the reference raised to it, o and l rescaled and the half
+//    recomputed.  p <= 2^16 stays far inside fp32 and bf16 range and o / l is unchanged.
 //  * O^T = V^T P^T: P^T is the B operand exactly as the S^T accumulators sit in
 //    registers (the contraction order over keys is permuted to match), V^T is read
-//    from a row-major LDS tile with ds_read_b64_tr_b16.  A lane owns one query, so
-//    the rescale factor is a per-lane scalar.
+//    from a row-major LDS tile with ds_read_b64_tr_b16.  A lane owns one query, so the
+//    rescale factor is a per-lane scalar.
 //  * Logits are in the base-2 domain: RoPE'd q is pre-multiplied by log2(e)/sqrt(d_h)
 //    before rounding to bf16, so p = exp2(s - m).
 //  * K and V move from HBM to LDS with direct 16-byte loads (global_load_lds_dwordx4),
 //    so no registers are tied up by loads in flight.  V lands in its final, xor-swizzled
-//    layout; K lands in a staging area and each thread rotates the chunks it loaded
-//    (RoPE at load) into the padded K tile.  The rotation angles advance from block
-//    to block by angle addition and are re-derived exactly (fp64 reduction) every 16
-//    blocks.
-//  * K/V blocks are double-buffered; the next block's loads are in flight while the
-//    current one is consumed.  Work is ordered longest-first for causal load balance
-//    and mapped so all query blocks of one KV head land on one XCD (shared L2).
+//    layout; raw K lands in a staging area and each thread rotates the chunks it loaded
+//    (RoPE at load) into the padded K tile.  The rotation angles advance from block to
+//    block by angle addition and are re-derived exactly (fp64 reduction) every 16 blocks.
+//  * Raw K is loaded two blocks ahead and V one block ahead; the rotation of block j+1
+//    happens during block j.  Work is ordered longest-first for causal load balance and
+//    mapped so all query blocks of one KV head land on one XCD (shared L2).
 #include <math.h>
 
 #include <type_traits>
@@ -290,19 +293,24 @@ void fwd_bf16_kernel(FwdParams p) {
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
         s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_op, bop, acc, 0, 0, 0);
       }
+    bf16x8 aop[C::KS][2];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) aop[ks][mb] = *(const bf16x8*)(kb + (mb * 32 + l32) * C::KSTR + ks * 16 + g * 8);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a = *(const bf16x8*)(kb + (mb * 32 + l32) * C::KSTR + ks * 16 + g * 8);
+        const bf16x8 a = aop[ks][mb];
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
           s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[nb][ks], s[mb][nb], 0, 0, 0);
       }
     }
   };
-  // exp2 of one 32-key half for both n-blocks -> bf16 P operands, row sums.
-  auto expo = [&](f32x16 (&s)[2][kNB], int mb, bf16x8 (&pop)[kNB][4]) {
+  // exp2 of one 32-key half for both n-blocks -> bf16 P operands and this half's row sums.
+  auto expo = [&](f32x16 (&s)[2][kNB], int mb, bf16x8 (&pop)[kNB][4], float (&lt)[kNB]) {
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       float lsum = 0.f;
@@ -318,24 +326,30 @@ void fwd_bf16_kernel(FwdParams p) {
         }
         pop[nb][mb * 2 + h] = __builtin_bit_cast(bf16x8, pk);
       }
-      l_run[nb] += lsum;
+      lt[nb] = lsum;
     }
   };
   const int a16 = lane / 16, lam = lane % 16;
-  // O^T += V^T P^T for one 16-key step.
-  auto pv = [&](const char* vb, int kstep, const bf16x8 (&pop)[kNB][4]) {
-    const int r1 = kstep * 16 + 4 * g + lam / 4;  // rows of the two transpose reads
-    const int r2 = r1 + 8;
+  // O^T += V^T P^T for one 16-key step.  The transpose-read byte offsets of each 32-dim
+  // block are the same for every key step up to a constant (the swizzle only depends on
+  // row % 4), so they are computed once.
+  int toff[C::DB];
+  {
+    const int r1 = 4 * g + lam / 4;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
       const int col = db * 32 + 16 * (a16 % 2) + 4 * (lam % 4);  // first of 4 dims
       const int c = col / 8, half = (col % 8) / 4;
-      const int off1 = (r1 * C::CPR + (c ^ vswz<D>(r1))) * 16 + half * 8;
-      const int off2 = (r2 * C::CPR + (c ^ vswz<D>(r2))) * 16 + half * 8;
-      const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(vb + off1));
+      toff[db] = (r1 * C::CPR + (c ^ vswz<D>(r1))) * 16 + half * 8;
+    }
+  }
+  auto pv = [&](const char* vb, int kstep, const bf16x8 (&pop)[kNB][4]) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const char* p1 = vb + toff[db] + kstep * 16 * C::CPR * 16;
+      const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
       const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(vb + off2));
+          (__attribute__((address_space(3))) s16x4*)(p1 + 8 * C::CPR * 16));
       const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
       const bf16x8 a = __builtin_bit_cast(bf16x8, (u32x4){w0[0], w0[1], w1[0], w1[1]});
 #pragma unroll
@@ -378,56 +392,53 @@ void fwd_bf16_kernel(FwdParams p) {
             }
         }
       }
-      // block max (relative to the reference the product subtracted); raise the
-      // reference only when it is exceeded by more than 8
-      bool need[kNB];
-      float tabs[kNB];
-      bool any_need = false;
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        float t0 = max3(s[0][nb][0], s[0][nb][1], s[0][nb][2]);
-        float t1 = max3(s[1][nb][0], s[1][nb][1], s[1][nb][2]);
-#pragma unroll
-        for (int r = 3; r < 15; r += 2) {
-          t0 = max3(t0, s[0][nb][r], s[0][nb][r + 1]);
-          t1 = max3(t1, s[1][nb][r], s[1][nb][r + 1]);
-        }
-        float tmax = max3(t0, s[0][nb][15], fmaxf(t1, s[1][nb][15]));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-        tabs[nb] = tmax + bias;
-        need[nb] = tabs[nb] > m_ref[nb] + 8.f;
-        any_need |= need[nb];
-      }
-      if (__any(any_need)) {
-        __asm__ volatile("");  // keep this rare path a real branch (no speculation)
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-          const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-          const float m_new = need[nb] ? bf16_ceil(tabs[nb]) : m_ref[nb];
-          const float alpha = need[nb] ? fast_exp2(m_ref[nb] - m_new) : 1.f;  // 0 when m_ref was -inf
-          const float delta = need[nb] ? m_new - bias : 0.f;
-          l_run[nb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][nb][r] *= alpha;
-          m_ref[nb] = m_new;
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[mb][nb][r] -= delta;
-        }
-      }
-      // probabilities and O^T += V^T P^T; the exponentials of the second key half run
-      // under the products of the first
+      // Probabilities with the current reference (the product already subtracted it), one
+      // 32-key half at a time; O^T += V^T P^T for that half.  The exact block max is only
+      // needed when a row has no reference yet or a half's row sum exceeds 2^16 (the
+      // reference is stale by more than ~16): then the reference is raised to the max
+      // (bf16-exact), o and l are rescaled, and the half is recomputed.
       bf16x8 pop[kNB][4];
-      expo(s, 0, pop);
-      pv(vbuf, 0, pop);
-      pv(vbuf, 1, pop);
-      expo(s, 1, pop);
-      pv(vbuf, 2, pop);
-      pv(vbuf, 3, pop);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        float lt[kNB];
+        expo(s, mb, pop, lt);
+        bool bad = false;
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) bad |= (m_ref[nb] == -INFINITY) || !(lt[nb] <= 65536.f);
+        if (__any(bad)) {
+          __asm__ volatile("");  // keep this rare path a real branch (no speculation)
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb) {
+            float tmax = max3(s[mb][nb][0], s[mb][nb][1], s[mb][nb][2]);
+#pragma unroll
+            for (int r = 3; r < 15; r += 2) tmax = max3(tmax, s[mb][nb][r], s[mb][nb][r + 1]);
+            tmax = fmaxf(tmax, s[mb][nb][15]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
+            const float tabs = tmax + bias;
+            const bool need = tabs > m_ref[nb] + 8.f;
+            const float m_new = need ? bf16_ceil(tabs) : m_ref[nb];
+            const float alpha = need ? fast_exp2(m_ref[nb] - m_new) : 1.f;  // 0 when m_ref was -inf
+            const float delta = need ? m_new - bias : 0.f;
+            l_run[nb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[db][nb][r] *= alpha;
+            m_ref[nb] = m_new;
+            // this half and the next one were computed against the old reference
+#pragma unroll
+            for (int mm = mb; mm < 2; ++mm)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) s[mm][nb][r] -= delta;
+          }
+          expo(s, mb, pop, lt);
+        }
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) l_run[nb] += lt[nb];
+        pv(vbuf, 2 * mb, pop);
+        pv(vbuf, 2 * mb + 1, pop);
+      }
     } else if (rot) {
       rotate_k(it + 1, std::integral_constant<int, PAR ^ 1>{});
     }
