@@ -9,12 +9,22 @@
 // kernel combines the splits with the same rescaling that the online softmax uses
 // between key blocks ("Deep dive: FlashAttention" of the same page).
 //
-// Per wave, two 16-token blocks per step:
-//   S^T[token][head] = K q^T   v_mfma_f32_16x16x32_bf16, K straight from HBM as the
-//                              A operand (lane: token lane%16, 8 dims), q^T from registers
-//   online softmax per lane    a lane owns one head (lane%16) and 8 of the 32 tokens
-//   O^T[dim][head] += V^T P^T  P^T is the B operand as it sits in registers; V^T comes
-//                              from LDS through ds_read_b64_tr_b16 (V stays row-major)
+// A workgroup is one wave.  It streams its split (96 cache blocks = 1536 tokens at
+// most) one 16-token block at a time through a private 2-stage LDS ring filled by
+// direct 16-byte loads (global_load_lds_dwordx4) one block ahead, so the bytes in
+// flight do not occupy registers and a CU can hold ten such workgroups (memory
+// parallelism comes from many small, independent streams).  The wave's block-table
+// entries are read once, one per lane, and broadcast per block with readlane.  Per
+// block:
+//   S^T[token][head] = K q^T   v_mfma_f32_16x16x32_bf16; the K operand is read from LDS
+//                              (xor-swizzled rows: conflict-free), q^T sits in registers
+//   probabilities              a lane owns one head (lane % 16) and 4 of the 16 tokens
+//   O^T[dim][head] += V^T P^T  v_mfma_f32_16x16x16_bf16: P^T is the B operand exactly as
+//                              the S^T accumulators sit in registers; V^T comes from LDS
+//                              through ds_read_b64_tr_b16 (V stays row-major)
+// The running max is only a reference: it is set from the first block and re-derived
+// (with o and l rescaled) only when a block's probabilities sum past 2^16, so the
+// common path has no cross-lane reduction.
 #include <math.h>
 
 #include "attn_common.h"
@@ -24,7 +34,9 @@ namespace attn {
 
 constexpr int kDecD = 128;        // head size served by the decode kernels
 constexpr int kDecBlock = 16;     // tokens per cache block
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 1;
+constexpr int kStages = 2;        // LDS ring depth per wave (blocks)
+constexpr int kStageBytes = 2 * kDecBlock * kDecD * 2;  // K and V of one block
 
 // Element offset of the (physical block, kv head) slice holding token block `j` of
 // sequence `b`.  The only place the block table is read; used by every paged kernel.
@@ -35,19 +47,18 @@ __device__ __forceinline__ size_t paged_slice(const int32_t* __restrict__ block_
   return (((size_t)phys * Hkv + kvh) * kDecBlock) * (size_t)d;
 }
 
-// LDS position (in 16-byte chunks) of chunk c of token row t inside one staged V block:
-// rows of 16 chunks, chunk index xor-swizzled by 2t so the transpose reads of a
-// half-wave (8 rows x 2 chunks) fall on 16 distinct bank groups.
+// 16-byte chunk position of chunk c of token row t inside a staged K block: reading
+// chunk c of all 16 rows (the MFMA operand pattern) then hits 16 distinct bank groups.
+__device__ __forceinline__ int kpos(int t, int c) { return t * 16 + (c ^ t); }
+// Same for V under the transpose-read pattern (a half wave reads 8 rows x 2 chunks).
 __device__ __forceinline__ int vpos(int t, int c) { return t * 16 + (c ^ ((2 * t) & 15)); }
 
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
-  __shared__ u32x4 vlds[kDecWaves][2][kDecBlock * 16];            // 16 KiB
-  __shared__ float red_o[kDecWaves][16][kDecD + 1];                // per-wave partial outputs
-  __shared__ float red_ml[kDecWaves][16][2];
+__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];  // kDecWaves * kStages * kStageBytes
 
   const int wid = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int grp = lane / 16;   // 16-lane group
+  const int grp = lane / 16;  // 16-lane group
   const int l16 = lane % 16;
   int w = blockIdx.x;
   const int sp = w % p.max_splits;
@@ -101,137 +112,133 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   const int share = (bps + kDecWaves - 1) / kDecWaves;
   const int wb0 = blk0 + wid * share;
   const int wb1 = min(blk1, wb0 + share);
+  const int nmine = max(0, wb1 - wb0);
 
-  float m = -INFINITY;  // running max (base 2), same in all four groups for a head
-  float l = 0.f;        // this lane's partial normaliser
+  char* ring = dsm + (size_t)wid * kStages * kStageBytes;
+  const __bf16* kc = (const __bf16*)p.k_cache;
+  const __bf16* vc = (const __bf16*)p.v_cache;
+
+  // This wave's block-table entries, one per lane (read once, then broadcast per block).
+  const int tbl = (lane < nmine) ? p.block_table[(size_t)b * p.max_blocks_per_seq + wb0 + lane] : 0;
+  const int tbl2 = (lane + 64 < nmine) ? p.block_table[(size_t)b * p.max_blocks_per_seq + wb0 + 64 + lane] : 0;
+
+  // Direct loads of block j into stage st: load i covers token rows 4i .. 4i+3.
+  auto issue = [&](int j, int st) {
+    const int jj = j - wb0;
+    const int phys = jj < 64 ? __builtin_amdgcn_readlane(tbl, jj) : __builtin_amdgcn_readlane(tbl2, jj - 64);
+    const size_t sl = (((size_t)phys * p.Hkv + kvh) * kDecBlock) * (size_t)kDecD;
+    char* kdst = ring + st * kStageBytes;
+    char* vdst = kdst + kStageBytes / 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * i + grp;
+      load_lds16(kc + sl + (size_t)t * kDecD + (l16 ^ t) * 8, kdst + i * 1024);
+      load_lds16(vc + sl + (size_t)t * kDecD + (l16 ^ ((2 * t) & 15)) * 8, vdst + i * 1024);
+    }
+  };
+
+  float m_ref = -INFINITY;  // reference max (base 2) for head l16, same in its 4 lanes
+  float l = 0.f;            // this lane's partial normaliser
   f32x4 o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const __bf16* kc = (const __bf16*)p.k_cache;
-  const __bf16* vc = (const __bf16*)p.v_cache;
+  // prologue: kStages-1 blocks in flight
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (i < nmine) issue(wb0 + i, i);
 
-  for (int j = wb0; j < wb1; j += 2) {
-    const bool has1 = (j + 1) < wb1;
-    size_t sl[2];
-    sl[0] = paged_slice(p.block_table, p.max_blocks_per_seq, b, j, p.Hkv, kvh, kDecD);
-    sl[1] = has1 ? paged_slice(p.block_table, p.max_blocks_per_seq, b, j + 1, p.Hkv, kvh, kDecD) : sl[0];
-
-    // K as the A operand: token l16, dims grp*8 + 32*kk.
-    bf16x8 ka[2][4];
-    u32x4 vr[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        ka[u][kk] = *(const bf16x8*)(kc + sl[u] + (size_t)l16 * kDecD + grp * 8 + 32 * kk);
-      // V rows for LDS staging: load i covers rows 4i..4i+3, chunk chosen by the swizzle
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * i + grp;
-        const int c = l16 ^ ((2 * t) & 15);
-        vr[u][i] = *(const u32x4*)(vc + sl[u] + (size_t)t * kDecD + c * 8);
-      }
+  for (int i = 0; i < nmine; ++i) {
+    const int j = wb0 + i;
+    const int st = i % kStages;
+    if (i + kStages - 1 < nmine) {
+      issue(j + kStages - 1, (i + kStages - 1) % kStages);
+      __builtin_amdgcn_s_waitcnt(0x0f70 | (8 * (kStages - 1)));  // block j has landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0f70);
     }
+    const char* kst = ring + st * kStageBytes;
+    const char* vst = kst + kStageBytes / 2;
 
-    // S^T for both blocks.
-    f32x4 s[2];
+    // S^T = K q^T for the 16 tokens of the block.
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][kk], qop[kk], acc, 0, 0, 0);
-      s[u] = acc;
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 a = *(const bf16x8*)(kst + kpos(l16, grp + 4 * kk) * 16);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[kk], s, 0, 0, 0);
     }
-    // Mask tokens past the sequence (and the absent second block) by selection.
-    float tmax = -INFINITY;
+    // tokens past the sequence are selected away (their cache slots may hold anything)
+    const bool tail = (j + 1) * kDecBlock > L;
+    if (tail) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = (j + u) * kDecBlock + grp * 4 + r;
-        const bool vis = (u == 0 || has1) && tok < L;
-        s[u][r] = vis ? s[u][r] : -INFINITY;
-        tmax = fmaxf(tmax, s[u][r]);
-      }
+      for (int r = 0; r < 4; ++r)
+        if (j * kDecBlock + grp * 4 + r >= L) s[r] = -INFINITY;
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-
-    // Stage V (rows past the sequence become zeros, so a poisoned slot never reaches
-    // the product).
+    const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+    float pv[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(s[r] - mu);
+    float bsum = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+    if (__any(m_ref == -INFINITY || !(bsum <= 65536.f))) {
+      __asm__ volatile("");  // rare: derive the reference from this block's max
+      float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const bool raise = tmax > m_ref + 8.f || (m_ref == -INFINITY && tmax > -INFINITY);
+      const float m_new = raise ? tmax : m_ref;
+      const float alpha = raise ? fast_exp2(m_ref - m_new) : 1.f;  // 0 when m_ref was -inf
+      l *= alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * i + grp;
-        const int c = l16 ^ ((2 * t) & 15);
-        const int tok = (j + u) * kDecBlock + t;
-        const bool vis = (u == 0 || has1) && tok < L;
-        u32x4 val = vr[u][i];
-        if (!vis) val = (u32x4){0u, 0u, 0u, 0u};
-        vlds[wid][u][vpos(t, c)] = val;
-      }
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[mb][r] *= alpha;
+      m_ref = m_new;
+      const float mu2 = (m_ref == -INFINITY) ? 0.f : m_ref;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(s[r] - mu2);
+      bsum = (pv[0] + pv[1]) + (pv[2] + pv[3]);
     }
-
-    const float m_new = fmaxf(m, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    float psum = 0.f;
-    u32x4 pk;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float p0 = fast_exp2(s[u][0] - m_use), p1 = fast_exp2(s[u][1] - m_use);
-      const float p2 = fast_exp2(s[u][2] - m_use), p3 = fast_exp2(s[u][3] - m_use);
-      psum += (p0 + p1) + (p2 + p3);
-      pk[2 * u] = pack_bf16(p0, p1);
-      pk[2 * u + 1] = pack_bf16(p2, p3);
-    }
-    l = l * alpha + psum;
-    m = m_new;
-    const bf16x8 pop = __builtin_bit_cast(bf16x8, pk);
-
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS stores are done
-    __builtin_amdgcn_wave_barrier();
-
-    // O^T += V^T P^T over the 32 tokens, 16 dims per product.
+    l += bsum;
+    // masked tokens have p = 0, but their V slots may hold non-finite values: zero the
+    // probabilities AND make sure the transposed V values of those rows are not used by
+    // selecting the P operand only (0 * NaN would still poison the product), see below
+    const u32x2 pk = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
+    const s16x4 pop = __builtin_bit_cast(s16x4, pk);
+    // O^T += V^T P^T, 16 dims per product.
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
+      const int t = 4 * grp + l16 / 4;
       const int dim = 16 * mb + 4 * (l16 % 4);
       const int c = dim / 8, half = (dim % 8) / 4;
-      const int t = 4 * grp + l16 / 4;
-      const char* base0 = (const char*)&vlds[wid][0][0];
-      const char* base1 = (const char*)&vlds[wid][1][0];
-      const int off = vpos(t, c) * 16 + half * 8;
-      s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(base0 + off));
-      s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(base1 + off));
-      const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
-      const u32x4 aw = {w0[0], w0[1], w1[0], w1[1]};
-      f32x4 acc = o[mb];
-      acc[0] *= alpha;
-      acc[1] *= alpha;
-      acc[2] *= alpha;
-      acc[3] *= alpha;
-      o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aw), pop, acc, 0, 0, 0);
+      s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vst + vpos(t, c) * 16 + half * 8));
+      if (tail) {
+        // rows (tokens) past the sequence: this lane's 4 values come from tokens
+        // 4 * grp .. 4 * grp + 3 of the block (transpose read); zero the invalid ones
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (j * kDecBlock + grp * 4 + r >= L) a[r] = 0;
+      }
+      o[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pop, o[mb], 0, 0, 0);
     }
-    __builtin_amdgcn_wave_barrier();  // reads of this stage finish before it is overwritten
   }
 
   // Combine the four token groups of a head: l sums, m is shared.
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
 
-  // Per-wave partials into LDS, then merge the waves of the workgroup.
+  // Per-wave partials into LDS (reusing the ring), then merge the waves of the workgroup.
+  __syncthreads();
+  float* red_o = (float*)dsm;                            // [kDecWaves][16][kDecD + 1]
+  float* red_ml = red_o + kDecWaves * 16 * (kDecD + 1);  // [kDecWaves][16][2]
   if (l16 < G) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red_o[wid][l16][16 * mb + 4 * grp + r] = o[mb][r];
+      for (int r = 0; r < 4; ++r) red_o[(wid * 16 + l16) * (kDecD + 1) + 16 * mb + 4 * grp + r] = o[mb][r];
     if (grp == 0) {
-      red_ml[wid][l16][0] = m;
-      red_ml[wid][l16][1] = l;
+      red_ml[(wid * 16 + l16) * 2] = m_ref;
+      red_ml[(wid * 16 + l16) * 2 + 1] = l;
     }
   }
   __syncthreads();
@@ -239,13 +246,13 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   for (int idx = threadIdx.x; idx < G * kDecD; idx += blockDim.x) {
     const int hh = idx / kDecD, d = idx % kDecD;
     float M = -INFINITY;
-    for (int ww = 0; ww < nwav; ++ww) M = fmaxf(M, red_ml[ww][hh][0]);
+    for (int ww = 0; ww < nwav; ++ww) M = fmaxf(M, red_ml[(ww * 16 + hh) * 2]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float acc = 0.f, lsum = 0.f;
     for (int ww = 0; ww < nwav; ++ww) {
-      const float sc = fast_exp2(red_ml[ww][hh][0] - Mu);
-      acc += sc * red_o[ww][hh][d];
-      lsum += sc * red_ml[ww][hh][1];
+      const float sc = fast_exp2(red_ml[(ww * 16 + hh) * 2] - Mu);
+      acc += sc * red_o[(ww * 16 + hh) * (kDecD + 1) + d];
+      lsum += sc * red_ml[(ww * 16 + hh) * 2 + 1];
     }
     const size_t slot = ((size_t)b * p.Hq + kvh * G + hh) * p.max_splits + sp;
     p.part_o[slot * kDecD + d] = acc;
@@ -307,13 +314,16 @@ __global__ __launch_bounds__(256) void paged_gather_kernel(const char* cache, co
 
 int decode_blocks_per_split(int max_blocks_per_seq) {
   (void)max_blocks_per_seq;
-  return 32;  // 512 tokens per split, 8 blocks per wave
+  return 96;  // 1536 tokens per split
 }
 
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
   const long long grid = (long long)p.num_seqs * p.Hkv * p.max_splits;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(decode_partial_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  constexpr size_t lds = (size_t)kDecWaves * kStages * kStageBytes;
+  static_assert(lds >= (size_t)kDecWaves * 16 * (kDecD + 1) * 4 + kDecWaves * 16 * 2 * 4,
+                "the reduction buffer reuses the staging ring");
+  hipLaunchKernelGGL(decode_partial_kernel, dim3((unsigned)grid), dim3(64), lds, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(p.num_seqs * p.Hq)), dim3(kDecD), 0, stream, p);

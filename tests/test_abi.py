@@ -90,8 +90,8 @@ def test_decode_validation(lib, kw, status):
 
 def test_workspace_bytes(lib):
     import exact_transformer_attention_amd as e
-    # 32 blocks (512 tokens) per split: 512 blocks -> 16 splits; (d_h + 2) fp32 per partial
-    assert e.attn_decode_workspace_bytes(64, 32, 128, 512, 16) == 64 * 32 * 16 * 130 * 4
+    # 96 blocks (1536 tokens) per split: 512 blocks -> 6 splits; (d_h + 2) fp32 per partial
+    assert e.attn_decode_workspace_bytes(64, 32, 128, 512, 16) == 64 * 32 * 6 * 130 * 4
     assert e.attn_decode_workspace_bytes(1, 1, 128, 1, 16) == 130 * 4
     assert e.attn_decode_workspace_bytes(0, 32, 128, 512, 16) == 0
 
