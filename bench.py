@@ -55,6 +55,64 @@ def measured_traffic(kind, digest):
     return t.get("hbm_bytes_per_launch")
 
 
+def summarize_pmc(fetch_csv, write_csv, out_dir):
+    """Per-launch HBM traffic of the timed kernels from two rocprofv3 --pmc runs (FETCH_SIZE,
+    then WRITE_SIZE; kilobytes per dispatch), scaled by the factor the same counters read
+    for a plain 1 GiB device copy (run with --copy-calibration).  Writes
+    profiles/traffic.json (read back by the benchmark line) and a readable summary."""
+    import collections
+    import csv
+
+    def per_kernel(path, counter):
+        rows = list(csv.DictReader(open(path)))
+        disp = collections.defaultdict(float)
+        name = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            disp[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            name[r["Dispatch_Id"]] = r["Kernel_Name"]
+        by = collections.defaultdict(list)
+        for d, v in disp.items():
+            by[name[d]].append(v * 1024.0)  # KiB -> bytes
+        return by
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(by, key):
+        vals = [v for k, vs in by.items() if key in k for v in vs]
+        return sum(vals) / len(vals) if vals else None
+
+    copy_bytes = float(1 << 30)
+
+    def calib(by):
+        # the calibration copies are the three largest device-copy dispatches
+        vals = sorted((v for k, vs in by.items() if "copyBuffer" in k for v in vs), reverse=True)[:3]
+        return sorted(vals)[len(vals) // 2] if vals else None
+
+    f_copy = calib(fetch)
+    w_copy = calib(write)
+    f_scale = copy_bytes / f_copy if f_copy else 1.0
+    w_scale = copy_bytes / w_copy if w_copy else 1.0
+    res = {"calibration": {"kernel": "1 GiB device copy", "fetch_raw_bytes": f_copy, "write_raw_bytes": w_copy,
+                           "fetch_scale": f_scale, "write_scale": w_scale}}
+    for kind, keys, srcs in (("prefill", ["fwd_bf16_kernel"], PREFILL_SOURCES),
+                             ("decode", ["decode_partial_kernel", "decode_merge_kernel"], DECODE_SOURCES)):
+        fb = [pick(fetch, k) for k in keys]
+        wb = [pick(write, k) for k in keys]
+        if any(x is None for x in fb + wb):
+            continue
+        rd = sum(fb) * f_scale
+        wr = sum(wb) * w_scale
+        res[kind] = {"kernels": keys, "fetch_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+                     "hbm_bytes_per_launch": rd + wr, "source_digest": kernel_sources_digest(srcs)}
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
 def cpu_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -64,28 +122,29 @@ def cpu_threads():
         return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline_prefill(cfg):
-    """The fp64 oracle on a bounded sample of the prefill workload: batch 0, the 8 query
-    heads of KV heads 0 and 1, all 8192 rows (row blocks of 1024, each with its full softmax)."""
+def cpu_baseline_prefill(cfg, n_kv=6):
+    """The fp64 oracle on a bounded sample of the prefill workload: batch 0, the query heads
+    of the first n_kv KV heads, all rows (row blocks of 1024, each with its full softmax)."""
     import numpy as np
     import oracle
     import workloads
     q, k, v = workloads.make_fwd_inputs(**cfg)
-    qs = q[:1, :8].double().numpy()
-    ks = k[:1, :2].double().numpy()
-    vs = v[:1, :2].double().numpy()
+    nq = n_kv * (cfg["Hq"] // cfg["Hkv"])
+    qs = q[:1, :nq].double().numpy()
+    ks = k[:1, :n_kv].double().numpy()
+    vs = v[:1, :n_kv].double().numpy()
     t0 = time.perf_counter()
     oracle.attention(qs, ks, vs, causal=cfg["causal"], rope_base=cfg["rope_base"], pos=cfg["pos"],
                      row_block=1024)
     dt = time.perf_counter() - t0
-    flops = workloads.fwd_flops(1, 8, cfg["T"], cfg["S"], cfg["d_h"], cfg["causal"])
+    flops = workloads.fwd_flops(1, nq, cfg["T"], cfg["S"], cfg["d_h"], cfg["causal"])
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cpu_threads(), kind="oracle",
                 seconds=round(dt, 3),
-                sample=f"batch 0, query heads 0-7 (KV heads 0-1), all {cfg['T']} rows x {cfg['S']} keys, "
+                sample=f"batch 0, query heads 0-{nq - 1} (KV heads 0-{n_kv - 1}), all {cfg['T']} rows x {cfg['S']} keys, "
                        f"fp64 numpy, 1024-row blocks; {flops:.3e} algorithmic FLOP")
 
 
-def cpu_baseline_decode(d, cfg, n_seqs=8):
+def cpu_baseline_decode(d, cfg, n_seqs=64):
     """The fp64 oracle on the first n_seqs sequences of the decode workload."""
     import oracle
     import workloads
@@ -110,7 +169,13 @@ def main():
                     help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="time only one part (profiling runs)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/traffic.json")
     a = ap.parse_args()
+    if a.traffic_from:
+        print(json.dumps(summarize_pmc(a.traffic_from[0], a.traffic_from[1], os.path.join(ROOT, "profiles")),
+                         indent=1))
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the kernels are "
               "single-GPU and no multi-GPU path is built.", file=sys.stderr)
