@@ -204,7 +204,7 @@ def main():
         dout = torch.empty_like(dq)
         dlse = torch.empty(dq.shape[:2], dtype=torch.float32, device=dev)
         from exact_transformer_attention_amd import attn_decode_workspace_bytes
-        ws = torch.empty(attn_decode_workspace_bytes(dcfg["num_seqs"], dcfg["Hq"], dcfg["d_h"],
+        ws = torch.empty(attn_decode_workspace_bytes(dcfg["num_seqs"], dcfg["Hq"], dcfg["Hkv"], dcfg["d_h"],
                                                      d["max_blocks_per_seq"], 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 

@@ -30,7 +30,7 @@ def _load():
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp,
                                       vp, sz, i32, vp]
     lib.attn_decode_paged.restype = i32
-    lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_paged_gather.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.attn_paged_gather.restype = i32
@@ -107,8 +107,8 @@ def attn_fwd(q, k, v, causal=False, rope_base=0.0, pos=0, out=None, lse=None, wa
     return out, lse
 
 
-def attn_decode_workspace_bytes(num_seqs, Hq, d_h, max_blocks_per_seq, block_size=16):
-    return int(LIB.attn_decode_workspace_bytes(num_seqs, Hq, d_h, max_blocks_per_seq, block_size))
+def attn_decode_workspace_bytes(num_seqs, Hq, Hkv, d_h, max_blocks_per_seq, block_size=16):
+    return int(LIB.attn_decode_workspace_bytes(num_seqs, Hq, Hkv, d_h, max_blocks_per_seq, block_size))
 
 
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, block_size=16, rope_base=0.0,
@@ -130,7 +130,7 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, block_size=16,
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
-    need = attn_decode_workspace_bytes(N, Hq, d, mbps, block_size)
+    need = attn_decode_workspace_bytes(N, Hq, Hkv, d, mbps, block_size)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     st = LIB.attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),

@@ -6,7 +6,7 @@
 #include <cmath>
 #include <cstring>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "launchers.h"
 
 namespace {
@@ -72,11 +72,14 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int d_h, int max_blocks_per_seq, int block_size) {
-  if (num_seqs < 1 || Hq < 1 || d_h < 1 || max_blocks_per_seq < 1 || block_size < 1) return 0;
-  const int bps = attn::decode_blocks_per_split(max_blocks_per_seq);
-  const size_t splits = (size_t)((max_blocks_per_seq + bps - 1) / bps);
-  return (size_t)num_seqs * (size_t)Hq * splits * ((size_t)d_h + 2) * sizeof(float);
+size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_h, int max_blocks_per_seq,
+                                   int block_size) {
+  if (num_seqs < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d_h < 1 || max_blocks_per_seq < 1 ||
+      block_size < 1)
+    return 0;
+  const size_t slots = (size_t)attn::decode_num_slots(num_seqs, Hkv, max_blocks_per_seq);
+  const size_t parts = slots * (size_t)(Hq / Hkv);
+  return parts * ((size_t)d_h + 2) * sizeof(float) + ((size_t)num_seqs + 1) * sizeof(int32_t);
 }
 
 attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -92,7 +95,9 @@ attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* 
   if (bad_base(rope_base)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16 || d_h != 128 || block_size != 16 || Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
-  const size_t need = attn_decode_workspace_bytes(num_seqs, Hq, d_h, max_blocks_per_seq, block_size);
+  if ((long long)num_seqs * Hkv * max_blocks_per_seq > (1LL << 30) || (long long)num_seqs * Hq > (1LL << 30))
+    return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn_decode_workspace_bytes(num_seqs, Hq, Hkv, d_h, max_blocks_per_seq, block_size);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
 
   attn::DecodeParams p;
@@ -109,11 +114,11 @@ attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* 
   p.Hkv = Hkv;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.num_blocks = num_blocks;
-  p.blocks_per_split = attn::decode_blocks_per_split(max_blocks_per_seq);
-  p.max_splits = (max_blocks_per_seq + p.blocks_per_split - 1) / p.blocks_per_split;
-  const size_t nparts = (size_t)num_seqs * Hq * p.max_splits;
+  p.nwaves = attn::decode_num_waves(num_seqs, Hkv, max_blocks_per_seq);
+  const size_t nparts = (size_t)attn::decode_num_slots(num_seqs, Hkv, max_blocks_per_seq) * (size_t)(Hq / Hkv);
   p.part_o = (float*)workspace;
   p.part_ml = (float*)workspace + nparts * d_h;
+  p.seq_prefix = (int32_t*)(p.part_ml + nparts * 2);
   p.use_rope = rope_base > 0.f;
   fill_rope(p.rope_c, d_h, p.use_rope ? rope_base : 1.f);
   hipError_t e = attn::launch_decode_paged(p, (hipStream_t)stream);

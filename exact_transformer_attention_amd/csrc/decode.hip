@@ -3,19 +3,24 @@
 // "Self-Attention Complexity, FlashAttention, PagedAttention, and RoPE in Code"
 // (Part 3) describes the cache as fixed-size blocks located through a per-sequence
 // block table; "Why is attention O(n^2) ..." notes that a decode step must read the
-// whole KV cache and is memory-bound.  The work is therefore cut along the key axis:
-// workgroup (sequence, KV head, split) reads its split's blocks once, serves all query
-// heads that share the KV head, and leaves an unnormalised partial (o, m, l); a second
-// kernel combines the splits with the same rescaling that the online softmax uses
-// between key blocks ("Deep dive: FlashAttention" of the same page).
+// whole KV cache and is memory-bound.  The work is therefore cut along the key axis
+// into pieces that run in parallel, each leaving an unnormalised partial (o, m, l); a
+// second kernel combines the pieces of a (sequence, head) with the same rescaling the
+// online softmax uses between key blocks ("Deep dive: FlashAttention" of that page).
 //
-// A workgroup is one wave.  It streams its split (96 cache blocks = 1536 tokens at
-// most) one 16-token block at a time through a private 2-stage LDS ring filled by
-// direct 16-byte loads (global_load_lds_dwordx4) one block ahead, so the bytes in
-// flight do not occupy registers and a CU can hold ten such workgroups (memory
-// parallelism comes from many small, independent streams).  The wave's block-table
-// entries are read once, one per lane, and broadcast per block with readlane.  Per
-// block:
+// Work division.  All (sequence, KV head, cache block) triples are laid end to end
+// (sequence-major, then KV head, then block) and cut into equal runs, one per wave of a
+// grid sized to stay resident, so every wave streams the same number of blocks whatever
+// the mix of sequence lengths.  A run that crosses the end of a (sequence, KV head)
+// segment becomes several pieces; each piece writes its own partial slot.  A wave looks
+// up the next piece, and loads its block-table entries and q, a few blocks before the
+// current piece ends, and the first block of a piece is loaded while the last block of
+// the previous one is processed, so piece boundaries do not drain the stream.
+//
+// A workgroup is one wave.  It streams its blocks through a private 2-stage LDS ring
+// filled by direct 16-byte loads (global_load_lds_dwordx4) one block ahead, so the
+// bytes in flight do not occupy registers.  Block-table entries are read 64 at a time,
+// one per lane, and broadcast per block with readlane.  Per block:
 //   S^T[token][head] = K q^T   v_mfma_f32_16x16x32_bf16; the K operand is read from LDS
 //                              (xor-swizzled rows: conflict-free), q^T sits in registers
 //   probabilities              a lane owns one head (lane % 16) and 4 of the 16 tokens
@@ -34,17 +39,24 @@ namespace attn {
 
 constexpr int kDecD = 128;        // head size served by the decode kernels
 constexpr int kDecBlock = 16;     // tokens per cache block
-constexpr int kDecWaves = 1;
-constexpr int kStages = 2;        // LDS ring depth per wave (blocks)
+constexpr int kStages = 2;        // LDS ring depth (blocks)
+static_assert(kStages == 2, "the producer below runs exactly one block ahead");
 constexpr int kStageBytes = 2 * kDecBlock * kDecD * 2;  // K and V of one block
+constexpr int kDecodeLds = kStages * kStageBytes + (kDecD / 2) * 8;  // ring + RoPE table
+
+// Element offset of the (physical block, kv head) slice of a cache [blocks, Hkv, 16, d].
+__device__ __forceinline__ size_t slice_offset(int phys, int Hkv, int kvh, int d) {
+  return (((size_t)phys * Hkv + kvh) * kDecBlock) * (size_t)d;
+}
 
 // Element offset of the (physical block, kv head) slice holding token block `j` of
-// sequence `b`.  The only place the block table is read; used by every paged kernel.
+// sequence `b`.  Used by the gather kernel; the decode kernel reads the same entries
+// 64 at a time and forms the same offset.
 __device__ __forceinline__ size_t paged_slice(const int32_t* __restrict__ block_table,
                                               int max_blocks_per_seq, int b, int j, int Hkv,
                                               int kvh, int d) {
   const int phys = block_table[(size_t)b * max_blocks_per_seq + j];
-  return (((size_t)phys * Hkv + kvh) * kDecBlock) * (size_t)d;
+  return slice_offset(phys, Hkv, kvh, d);
 }
 
 // 16-byte chunk position of chunk c of token row t inside a staged K block: reading
@@ -53,50 +65,149 @@ __device__ __forceinline__ int kpos(int t, int c) { return t * 16 + (c ^ t); }
 // Same for V under the transpose-read pattern (a half wave reads 8 rows x 2 chunks).
 __device__ __forceinline__ int vpos(int t, int c) { return t * 16 + (c ^ ((2 * t) & 15)); }
 
-__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
-  extern __shared__ __attribute__((aligned(16))) char dsm[];  // kDecWaves * kStages * kStageBytes
+// Cache blocks read for a sequence of L tokens (its table row bounds the count).
+__device__ __forceinline__ int seq_blocks(int L, int max_blocks_per_seq) {
+  return min((max(L, 0) + kDecBlock - 1) / kDecBlock, max_blocks_per_seq);
+}
 
-  const int wid = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
+// Block counts of all sequences, scanned across the wave.  Lane l owns sequences
+// l*q .. l*q+q-1 (q = ceil(num_seqs / 64)); excl is the number of blocks before them,
+// nb0 / L0 the block count and length of its first sequence.
+struct SeqScan {
+  int excl, nb0, L0, q, total;
+};
+__device__ __forceinline__ SeqScan scan_seqs(const int32_t* __restrict__ seq_lens, int num_seqs,
+                                             int mbps, int lane) {
+  SeqScan s;
+  s.q = (num_seqs + kWave - 1) / kWave;
+  s.nb0 = 0;
+  s.L0 = 0;
+  int tot = 0;
+  for (int i = 0; i < s.q; ++i) {
+    const int b = lane * s.q + i;
+    if (b < num_seqs) {
+      const int L = seq_lens[b];
+      const int nb = seq_blocks(L, mbps);
+      if (i == 0) {
+        s.nb0 = nb;
+        s.L0 = L;
+      }
+      tot += nb;
+    }
+  }
+  int inc = tot;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(inc, d);
+    if (lane >= d) inc += y;
+  }
+  s.excl = inc - tot;
+  s.total = __shfl(inc, kWave - 1);
+  return s;
+}
+
+// All (sequence, KV head, block) triples, laid end to end (sequence-major, then KV head,
+// then block), are cut into equal runs, one per wave; both kernels derive the run
+// length from the total.
+__device__ __forceinline__ int run_length(int total, int nwaves) { return (total + nwaves - 1) / nwaves; }
+
+// Lookahead, in blocks before the end of a piece, at which the next piece is looked up.
+constexpr int kLookahead = 3;
+
+// One contiguous stretch of blocks of one (sequence, KV head) segment inside one wave's
+// run; its partial result goes to slot wave + segment index (distinct for distinct
+// pieces, since both grow along the order).
+struct Piece {
+  int b, kvh, j0, n, L, slot;
+};
+
+__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
+  extern __shared__ __attribute__((aligned(16))) char ring[];  // kDecodeLds bytes
+
+  const int lane = threadIdx.x;
   const int grp = lane / 16;  // 16-lane group
   const int l16 = lane % 16;
-  int w = blockIdx.x;
-  const int sp = w % p.max_splits;
-  w /= p.max_splits;
-  const int kvh = w % p.Hkv;
-  const int b = w / p.Hkv;
-  const int L = p.seq_lens[b];
-  const int nblk = (L + kDecBlock - 1) / kDecBlock;
-  const int bps = p.blocks_per_split;
-  const int blk0 = sp * bps;
-  if (blk0 >= nblk) return;  // uniform over the workgroup
-  const int blk1 = min(nblk, blk0 + bps);
-  const int G = p.Hq / p.Hkv;
-  const int head = kvh * G + l16;  // valid when l16 < G
+  const int w = blockIdx.x;
+  const int Hkv = p.Hkv;
+  const int G = p.Hq / Hkv;
+  const int mbps = p.max_blocks_per_seq;
+  const int nwaves = (int)gridDim.x;
 
-  // q^T operand: lane holds head l16, dims grp*8 + 32*kk .. +7; rotated at L-1, with
-  // the base-2 softmax scale folded in.
-  bf16x8 qop[4];
-  {
-    const float qscale = kLog2e / sqrtf((float)kDecD);
+  // RoPE constants in LDS: each lane needs a lane-dependent subset, and indexed reads of
+  // the kernel arguments would be memory loads that wait for every load in flight.
+  double* rope_lds = (double*)(ring + kStages * kStageBytes);
+  rope_lds[lane] = p.rope_c[lane];
+  __syncthreads();
+
+  const SeqScan sc = scan_seqs(p.seq_lens, p.num_seqs, mbps, lane);
+  if (w == 0) {  // block offsets of every sequence, for the merge kernel
+    int acc = sc.excl;
+    for (int i = 0; i < sc.q; ++i) {
+      const int b = lane * sc.q + i;
+      if (b < p.num_seqs) {
+        p.seq_prefix[b] = acc;
+        acc += seq_blocks(p.seq_lens[b], mbps);
+      }
+    }
+    if (lane == 0) p.seq_prefix[p.num_seqs] = sc.total;
+  }
+  const int total = sc.total * Hkv;
+  const int per = run_length(total, nwaves);
+
+  // This wave's run [run_pos, run_end), taken piece by piece.
+  int run_pos = w * per;
+  const int run_end = min(total, run_pos + per);
+  auto next_piece = [&](Piece& pc) -> bool {
+    if (run_pos >= run_end) return false;
+    // sequence holding run_pos: the last lane whose first block is at or before it,
+    // then (more than 64 sequences) a walk over that lane's sequences
+    const unsigned long long below = __ballot(sc.excl * Hkv <= run_pos && lane * sc.q < p.num_seqs);
+    const int ls = 63 - __builtin_clzll(below);  // lane 0 always qualifies
+    int off = __builtin_amdgcn_readlane(sc.excl, ls) * Hkv;
+    int b = ls * sc.q;
+    int nb = __builtin_amdgcn_readlane(sc.nb0, ls);
+    int L = __builtin_amdgcn_readlane(sc.L0, ls);
+    while (run_pos >= off + nb * Hkv) {  // only when q > 1 (or empty sequences)
+      off += nb * Hkv;
+      ++b;
+      L = p.seq_lens[b];
+      nb = seq_blocks(L, mbps);
+    }
+    const int rel = run_pos - off;
+    pc.b = b;
+    pc.kvh = rel / nb;
+    pc.j0 = rel - pc.kvh * nb;
+    pc.n = min(run_end, off + (pc.kvh + 1) * nb) - run_pos;
+    pc.L = L;
+    pc.slot = w + b * Hkv + pc.kvh;
+    run_pos += pc.n;
+    return true;
+  };
+  auto table_row = [&](const Piece& pc) { return p.block_table + (size_t)pc.b * mbps + pc.j0; };
+  auto load_q = [&](const Piece& pc, u32x4* raw) {
+    const int head = pc.kvh * G + l16;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      raw[kk] = (u32x4){0u, 0u, 0u, 0u};
+      if (l16 < G)
+        raw[kk] = *(const u32x4*)((const __bf16*)p.q + ((size_t)pc.b * p.Hq + head) * kDecD + grp * 8 + 32 * kk);
+    }
+  };
+  // q^T operand: lane holds head l16, dims grp*8 + 32*kk .. +7, rotated at position
+  // L-1, with the base-2 softmax scale folded in.
+  const float qscale = kLog2e / sqrtf((float)kDecD);
+  auto rotate_q = [&](const u32x4* raw, int L, bf16x8* qop) {
     const int64_t qposn = (int64_t)L - 1;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (l16 < G) {
-        const u32x4* src = (const u32x4*)((const __bf16*)p.q + ((size_t)b * p.Hq + head) * kDecD +
-                                          grp * 8 + 32 * kk);
-        raw = *src;
-      }
       u32x4 packed;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x0 = bf16_lo(raw[e]), x1 = bf16_hi(raw[e]);
+        float x0 = bf16_lo(raw[kk][e]), x1 = bf16_hi(raw[kk][e]);
         if (p.use_rope) {
           const int pair = (grp * 8 + 32 * kk) / 2 + e;
-          const float turns = rope_turns(qposn, p.rope_c[pair]);
           float sn, cs;
-          sincos_rev(turns, &sn, &cs);
+          sincos_rev(rope_turns(qposn, rope_lds[pair]), &sn, &cs);
           const float y0 = x0 * cs - x1 * sn;
           const float y1 = x0 * sn + x1 * cs;
           x0 = y0;
@@ -106,58 +217,95 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
       }
       qop[kk] = __builtin_bit_cast(bf16x8, packed);
     }
-  }
+  };
 
-  // This wave's contiguous share of the split.
-  const int share = (bps + kDecWaves - 1) / kDecWaves;
-  const int wb0 = blk0 + wid * share;
-  const int wb1 = min(blk1, wb0 + share);
-  const int nmine = max(0, wb1 - wb0);
-
-  char* ring = dsm + (size_t)wid * kStages * kStageBytes;
   const __bf16* kc = (const __bf16*)p.k_cache;
   const __bf16* vc = (const __bf16*)p.v_cache;
-
-  // This wave's block-table entries, one per lane (read once, then broadcast per block).
-  const int tbl = (lane < nmine) ? p.block_table[(size_t)b * p.max_blocks_per_seq + wb0 + lane] : 0;
-  const int tbl2 = (lane + 64 < nmine) ? p.block_table[(size_t)b * p.max_blocks_per_seq + wb0 + 64 + lane] : 0;
-
-  // Direct loads of block j into stage st: load i covers token rows 4i .. 4i+3.
-  auto issue = [&](int j, int st) {
-    const int jj = j - wb0;
-    const int phys = jj < 64 ? __builtin_amdgcn_readlane(tbl, jj) : __builtin_amdgcn_readlane(tbl2, jj - 64);
-    const size_t sl = (((size_t)phys * p.Hkv + kvh) * kDecBlock) * (size_t)kDecD;
+  // Direct loads of the block at physical index phys (KV head kvh) into stage st: load r
+  // covers token rows 4r .. 4r+3.
+  auto issue = [&](int phys, int kvh, int st) {
+    const size_t sl = slice_offset(phys, Hkv, kvh, kDecD);
     char* kdst = ring + st * kStageBytes;
     char* vdst = kdst + kStageBytes / 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * i + grp;
-      load_lds16(kc + sl + (size_t)t * kDecD + (l16 ^ t) * 8, kdst + i * 1024);
-      load_lds16(vc + sl + (size_t)t * kDecD + (l16 ^ ((2 * t) & 15)) * 8, vdst + i * 1024);
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * r + grp;
+      load_lds16(kc + sl + (size_t)t * kDecD + (l16 ^ t) * 8, kdst + r * 1024);
+      load_lds16(vc + sl + (size_t)t * kDecD + (l16 ^ ((2 * t) & 15)) * 8, vdst + r * 1024);
     }
   };
 
+  // Three pieces are live: the consumer's (cp), the producer's (pp, one block ahead, so
+  // either cp or the piece after it) and the next one (np).  np is looked up a few
+  // blocks before the producer needs it, and its first table entries and q are loaded
+  // then (so they do not hold registers for the whole piece).
+  Piece cp, pp, np;
+  if (!next_piece(cp)) return;  // uniform over the workgroup
+  pp = cp;
+  int tcur = (lane < pp.n) ? table_row(pp)[lane] : 0;  // producer's table window
+  int tnxt = (64 + lane < pp.n) ? table_row(pp)[64 + lane] : 0;  // the following window
+  u32x4 qraw[4];
+  load_q(cp, qraw);
+  int np_state = 0;  // 0: not looked up yet, 1: np valid, 2: no more work
+  int tnp = 0;
+  u32x4 qraw_np[4];
+  auto fetch_np = [&]() {
+    if (next_piece(np)) {
+      np_state = 1;
+      tnp = (lane < np.n) ? table_row(np)[lane] : 0;
+      load_q(np, qraw_np);
+    } else {
+      np_state = 2;
+    }
+  };
+  if (cp.n <= kLookahead) fetch_np();
+  issue(__builtin_amdgcn_readlane(tcur, 0), pp.kvh, 0);
+  int pi = 1;          // next block of pp to issue
+  bool prod = true;    // producer still has blocks
+  int gstep = 0;       // consumer block counter over all pieces (ring stage parity)
+
+  bf16x8 qop[4];
+  rotate_q(qraw, cp.L, qop);
   float m_ref = -INFINITY;  // reference max (base 2) for head l16, same in its 4 lanes
   float l = 0.f;            // this lane's partial normaliser
   f32x4 o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  int ci = 0;  // block of cp being consumed
 
-  // prologue: kStages-1 blocks in flight
-#pragma unroll
-  for (int i = 0; i < kStages - 1; ++i)
-    if (i < nmine) issue(wb0 + i, i);
-
-  for (int i = 0; i < nmine; ++i) {
-    const int j = wb0 + i;
-    const int st = i % kStages;
-    if (i + kStages - 1 < nmine) {
-      issue(j + kStages - 1, (i + kStages - 1) % kStages);
-      __builtin_amdgcn_s_waitcnt(0x0f70 | (8 * (kStages - 1)));  // block j has landed
+  for (;;) {
+    // producer: issue the next block (possibly the first of the next piece)
+    // (at the top of a step the producer is always on the consumer's piece: it moves on
+    // only while the consumer takes that piece's last block)
+    if (prod && pi == pp.n) {
+      if (np_state == 0) fetch_np();  // only if the piece was shorter than the lookahead
+      if (np_state == 1) {
+        pp = np;
+        tcur = tnp;
+        pi = 0;
+      } else {
+        prod = false;
+      }
+    }
+    if (prod) {
+      if ((pi & 63) == 0 && pi > 0) {
+        // a real branch: a select would read tnxt (and wait for its load) every block
+        __asm__ volatile("");
+        tcur = tnxt;
+      }
+      issue(__builtin_amdgcn_readlane(tcur, pi & 63), pp.kvh, (gstep + 1) % kStages);
+      const bool refill = (pi & 63) == 0 && pi + 64 < pp.n;
+      ++pi;
+      __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): the block being consumed has landed
+      if (refill)  // next 64 table entries of the producer's piece
+        tnxt = (pi + 63 + lane < pp.n) ? table_row(pp)[pi + 63 + lane] : 0;
     } else {
       __builtin_amdgcn_s_waitcnt(0x0f70);
     }
-    const char* kst = ring + st * kStageBytes;
+
+    const int j = cp.j0 + ci;
+    const int L = cp.L;
+    const char* kst = ring + (gstep % kStages) * kStageBytes;
     const char* vst = kst + kStageBytes / 2;
 
     // S^T = K q^T for the 16 tokens of the block.
@@ -199,87 +347,128 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
       bsum = (pv[0] + pv[1]) + (pv[2] + pv[3]);
     }
     l += bsum;
-    // masked tokens have p = 0, but their V slots may hold non-finite values: zero the
-    // probabilities AND make sure the transposed V values of those rows are not used by
-    // selecting the P operand only (0 * NaN would still poison the product), see below
     const u32x2 pk = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
     const s16x4 pop = __builtin_bit_cast(s16x4, pk);
-    // O^T += V^T P^T, 16 dims per product.
+    // O^T += V^T P^T, 16 dims per product.  The eight transpose reads are issued from one
+    // asm block that also waits for them: the compiler cannot tell which LDS bytes a
+    // ds_read_b64_tr_b16 builtin reads, so it would wait for every direct-to-LDS load in
+    // flight (including the next block's) before it.
+    s16x4 va[8];
+    {
+      const int t = 4 * grp + l16 / 4;
+      const int x = (l16 % 4) / 2, half = l16 % 2;
+      const uint32_t vbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)vst;
+      uint32_t ad[8];
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) ad[mb] = vbase + vpos(t, 2 * mb + x) * 16 + half * 8;
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8\n\t"
+          "ds_read_b64_tr_b16 %1, %9\n\t"
+          "ds_read_b64_tr_b16 %2, %10\n\t"
+          "ds_read_b64_tr_b16 %3, %11\n\t"
+          "ds_read_b64_tr_b16 %4, %12\n\t"
+          "ds_read_b64_tr_b16 %5, %13\n\t"
+          "ds_read_b64_tr_b16 %6, %14\n\t"
+          "ds_read_b64_tr_b16 %7, %15\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(va[0]), "=&v"(va[1]), "=&v"(va[2]), "=&v"(va[3]), "=&v"(va[4]), "=&v"(va[5]),
+            "=&v"(va[6]), "=&v"(va[7])
+          : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+            "v"(ad[7]));
+    }
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
-      const int t = 4 * grp + l16 / 4;
-      const int dim = 16 * mb + 4 * (l16 % 4);
-      const int c = dim / 8, half = (dim % 8) / 4;
-      s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(vst + vpos(t, c) * 16 + half * 8));
+      s16x4 a = va[mb];
       if (tail) {
-        // rows (tokens) past the sequence: this lane's 4 values come from tokens
-        // 4 * grp .. 4 * grp + 3 of the block (transpose read); zero the invalid ones
+        // masked tokens have p = 0 but their V slots may hold non-finite values
+        // (0 * NaN would poison the product): this lane's 4 values come from tokens
+        // 4 * grp .. 4 * grp + 3 of the block; zero the invalid ones
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (j * kDecBlock + grp * 4 + r >= L) a[r] = 0;
       }
       o[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pop, o[mb], 0, 0, 0);
     }
-  }
+    ++gstep;
+    if (++ci < cp.n) {
+      if (np_state == 0 && cp.n - ci <= kLookahead) fetch_np();
+      continue;
+    }
 
-  // Combine the four token groups of a head: l sums, m is shared.
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-
-  // Per-wave partials into LDS (reusing the ring), then merge the waves of the workgroup.
-  __syncthreads();
-  float* red_o = (float*)dsm;                            // [kDecWaves][16][kDecD + 1]
-  float* red_ml = red_o + kDecWaves * 16 * (kDecD + 1);  // [kDecWaves][16][2]
-  if (l16 < G) {
+    // End of the consumer's piece: its partial (l summed over the four token groups of
+    // a head; m is shared by them).
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (l16 < G) {
+      const size_t ps = (size_t)cp.slot * G + l16;
+      float* po = p.part_o + ps * kDecD;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+      for (int mb = 0; mb < 8; ++mb) *(f32x4*)(po + 16 * mb + 4 * grp) = o[mb];
+      if (grp == 0) *(float2*)(p.part_ml + ps * 2) = make_float2(m_ref, l);
+    }
+    if (np_state != 1) break;
+    // the producer has moved on to np (its first block is in flight): consume it next
+    cp = np;
+    np_state = 0;
+    rotate_q(qraw_np, cp.L, qop);
+    m_ref = -INFINITY;
+    l = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red_o[(wid * 16 + l16) * (kDecD + 1) + 16 * mb + 4 * grp + r] = o[mb][r];
-    if (grp == 0) {
-      red_ml[(wid * 16 + l16) * 2] = m_ref;
-      red_ml[(wid * 16 + l16) * 2 + 1] = l;
-    }
-  }
-  __syncthreads();
-  const int nwav = min(kDecWaves, (blk1 - blk0 + share - 1) / share);
-  for (int idx = threadIdx.x; idx < G * kDecD; idx += blockDim.x) {
-    const int hh = idx / kDecD, d = idx % kDecD;
-    float M = -INFINITY;
-    for (int ww = 0; ww < nwav; ++ww) M = fmaxf(M, red_ml[(ww * 16 + hh) * 2]);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    float acc = 0.f, lsum = 0.f;
-    for (int ww = 0; ww < nwav; ++ww) {
-      const float sc = fast_exp2(red_ml[(ww * 16 + hh) * 2] - Mu);
-      acc += sc * red_o[(ww * 16 + hh) * (kDecD + 1) + d];
-      lsum += sc * red_ml[(ww * 16 + hh) * 2 + 1];
-    }
-    const size_t slot = ((size_t)b * p.Hq + kvh * G + hh) * p.max_splits + sp;
-    p.part_o[slot * kDecD + d] = acc;
-    if (d == 0) {
-      p.part_ml[slot * 2] = M;
-      p.part_ml[slot * 2 + 1] = lsum;
-    }
+    for (int i = 0; i < 8; ++i) o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    ci = 0;
+    if (cp.n <= kLookahead) fetch_np();
   }
 }
 
-// Log-sum-exp merge of the split partials of one (sequence, query head).
+// Log-sum-exp merge of the pieces of one (sequence, query head).
 __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
   const int bh = blockIdx.x;
   const int b = bh / p.Hq;
+  const int G = p.Hq / p.Hkv;
+  const int kvh = (bh % p.Hq) / G, hh = (bh % p.Hq) % G;
   const int d = threadIdx.x;
-  const int L = p.seq_lens[b];
-  const int nblk = (L + kDecBlock - 1) / kDecBlock;
-  const int nsp = (nblk + p.blocks_per_split - 1) / p.blocks_per_split;
-  const size_t base = (size_t)bh * p.max_splits;
-  float M = -INFINITY;
-  for (int i = 0; i < nsp; ++i) M = fmaxf(M, p.part_ml[(base + i) * 2]);
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  float acc = 0.f, lsum = 0.f;
-  for (int i = 0; i < nsp; ++i) {
-    const float sc = fast_exp2(p.part_ml[(base + i) * 2] - Mu);
-    lsum += sc * p.part_ml[(base + i) * 2 + 1];
-    acc += sc * p.part_o[(base + i) * kDecD + d];
+  const int nb = seq_blocks(p.seq_lens[b], p.max_blocks_per_seq);
+  const int g = b * p.Hkv + kvh;
+  // waves whose runs overlap this (sequence, KV head) segment
+  int w0 = 0, w1 = -1;
+  if (nb > 0) {
+    const int per = run_length(p.seq_prefix[p.num_seqs] * p.Hkv, p.nwaves);
+    const int s0 = p.seq_prefix[b] * p.Hkv + kvh * nb;
+    w0 = s0 / per;
+    w1 = (s0 + nb - 1) / per;
+  }
+  // Eight partials per round, their loads issued together; the running max rescales
+  // what was accumulated before (same recurrence as between key blocks).
+  const int nparts = w1 - w0 + 1;
+  float M = -INFINITY, acc = 0.f, lsum = 0.f;
+  for (int i0 = 0; i0 < nparts; i0 += 8) {
+    float2 ml[8];
+    float ov[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ml[k] = make_float2(-INFINITY, 0.f);
+      ov[k] = 0.f;
+      const int i = i0 + k;
+      if (i < nparts) {
+        const size_t ps = (size_t)(w0 + i + g) * G + hh;
+        ml[k] = *(const float2*)(p.part_ml + ps * 2);
+        ov[k] = p.part_o[ps * kDecD + d];
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) Mb = fmaxf(Mb, ml[k].x);
+    if (Mb == -INFINITY) continue;
+    const float sc0 = fast_exp2(M - Mb);  // 0 while nothing was accumulated
+    acc *= sc0;
+    lsum *= sc0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float sc = fast_exp2(ml[k].x - Mb);
+      lsum += sc * ml[k].y;
+      acc += sc * ov[k];
+    }
+    M = Mb;
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   ((__bf16*)p.out)[(size_t)bh * kDecD + d] = (__bf16)(acc * inv);
@@ -312,21 +501,23 @@ __global__ __launch_bounds__(256) void paged_gather_kernel(const char* cache, co
   }
 }
 
-int decode_blocks_per_split(int max_blocks_per_seq) {
-  (void)max_blocks_per_seq;
-  return 96;  // 1536 tokens per split
+int decode_num_waves(int num_seqs, int Hkv, int max_blocks_per_seq) {
+  const long long work = (long long)num_seqs * Hkv * max_blocks_per_seq;
+  return (int)(work < kDecodeWaves ? work : kDecodeWaves);
+}
+
+long long decode_num_slots(int num_seqs, int Hkv, int max_blocks_per_seq) {
+  return (long long)decode_num_waves(num_seqs, Hkv, max_blocks_per_seq) + (long long)num_seqs * Hkv;
 }
 
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
-  const long long grid = (long long)p.num_seqs * p.Hkv * p.max_splits;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  constexpr size_t lds = (size_t)kDecWaves * kStages * kStageBytes;
-  static_assert(lds >= (size_t)kDecWaves * 16 * (kDecD + 1) * 4 + kDecWaves * 16 * 2 * 4,
-                "the reduction buffer reuses the staging ring");
-  hipLaunchKernelGGL(decode_partial_kernel, dim3((unsigned)grid), dim3(64), lds, stream, p);
+  constexpr size_t lds = kDecodeLds;
+  hipLaunchKernelGGL(decode_partial_kernel, dim3((unsigned)p.nwaves), dim3(64), lds, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(p.num_seqs * p.Hq)), dim3(kDecD), 0, stream, p);
+  const long long grid = (long long)p.num_seqs * p.Hq;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)grid), dim3(kDecD), 0, stream, p);
   return hipGetLastError();
 }
 

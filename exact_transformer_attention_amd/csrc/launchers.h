@@ -20,17 +20,21 @@ struct DecodeParams {
   const int32_t* seq_lens;
   void* out;
   float* lse;  // may be null
-  float* part_o;    // [num_seqs, Hq, max_splits, d_h] fp32 normalised partial outputs
-  float* part_ml;   // [num_seqs, Hq, max_splits, 2] fp32 (max in base 2, normaliser)
+  float* part_o;      // [slots, Hq / Hkv, d_h] fp32 unnormalised outputs
+  float* part_ml;     // [slots, Hq / Hkv, 2] fp32 (reference max in base 2, normaliser)
+  int32_t* seq_prefix;  // [num_seqs + 1] cache blocks before each sequence (written by the kernel)
   int num_seqs, Hq, Hkv, max_blocks_per_seq, num_blocks;
-  int max_splits;
-  int blocks_per_split;
+  int nwaves;         // grid of the partial kernel: one wave per workgroup
   int use_rope;
   double rope_c[64];
 };
 
-// Split size used by the decode kernels, in cache blocks of 16 tokens.
-int decode_blocks_per_split(int max_blocks_per_seq);
+// Waves of the decode partial kernel: enough to fill the chip while all stay resident
+// (ten 16 KiB LDS rings per compute unit).
+constexpr int kDecodeWaves = 2048;
+int decode_num_waves(int num_seqs, int Hkv, int max_blocks_per_seq);
+// Partial-result slots the decode kernels may write for these sizes.
+long long decode_num_slots(int num_seqs, int Hkv, int max_blocks_per_seq);
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_paged_gather(const void* cache, const int32_t* block_table,
                                const int32_t* seq_lens, int num_seqs, int Hkv, int d_h,

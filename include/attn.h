@@ -90,13 +90,15 @@ ATTN_API attn_status_t attn_fwd(const void* q, const void* k, const void* v, voi
  *                every used table entry in [0, num_blocks) (not checked on the device)
  *   out          [num_seqs, Hq, d_h] dtype `dtype`;  lse [num_seqs, Hq] fp32 or NULL
  *   workspace    device scratch of at least attn_decode_workspace_bytes(...) bytes for
- *                the split-K partial results; caller-owned, contents need no clearing
+ *                the partial results; caller-owned, contents need no clearing; two calls
+ *                that overlap in time must not share one workspace
  *   dtype        ATTN_BF16 only (ATTN_F32 returns ATTN_ERR_UNSUPPORTED)
  *
- * Supported: block_size == 16, d_h == 128, Hq % Hkv == 0, Hq / Hkv <= 16.
- * The key range of each (sequence, KV head) is cut into splits that run in parallel;
- * a second kernel merges the partial (output, max, normaliser) triples with a
- * log-sum-exp merge.
+ * Supported: block_size == 16, d_h == 128, Hq % Hkv == 0, Hq / Hkv <= 16,
+ * num_seqs * Hkv * max_blocks_per_seq <= 2^30.
+ * All (sequence, KV head, block) triples are cut into equal runs read in parallel
+ * (split-K along the key axis, balanced whatever the length mix); a second kernel
+ * merges the partial (output, max, normaliser) triples with a log-sum-exp merge.
  */
 ATTN_API attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* block_table, const int32_t* seq_lens,
@@ -106,8 +108,8 @@ ATTN_API attn_status_t attn_decode_paged(const void* q, const void* k_cache, con
                                 attn_dtype_t dtype, void* stream);
 
 /* Bytes of workspace attn_decode_paged needs for these sizes (0 on invalid sizes). */
-ATTN_API size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int d_h, int max_blocks_per_seq,
-                                   int block_size);
+ATTN_API size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_h,
+                                   int max_blocks_per_seq, int block_size);
 
 /*
  * attn_paged_gather -- copy each sequence's cached rows into a contiguous buffer using

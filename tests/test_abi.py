@@ -82,6 +82,7 @@ def dec(lib, **kw):
     (dict(N=0), 1), (dict(Hq=30), 1), (dict(mbps=0), 1), (dict(nb=0), 1), (dict(bs=0), 1),
     (dict(base=-2.0), 1), (dict(dtype=5), 1),
     (dict(dtype=0), 2), (dict(d=64), 2), (dict(bs=32), 2), (dict(Hq=64, Hkv=2), 2),
+    (dict(N=1 << 20, mbps=1 << 12), 2),
     (dict(ws=None), 3), (dict(wsb=16), 3),
 ])
 def test_decode_validation(lib, kw, status):
@@ -90,10 +91,14 @@ def test_decode_validation(lib, kw, status):
 
 def test_workspace_bytes(lib):
     import exact_transformer_attention_amd as e
-    # 96 blocks (1536 tokens) per split: 512 blocks -> 6 splits; (d_h + 2) fp32 per partial
-    assert e.attn_decode_workspace_bytes(64, 32, 128, 512, 16) == 64 * 32 * 6 * 130 * 4
-    assert e.attn_decode_workspace_bytes(1, 1, 128, 1, 16) == 130 * 4
-    assert e.attn_decode_workspace_bytes(0, 32, 128, 512, 16) == 0
+    # partial slots: one per wave of the grid (at most 2048, at most one per block) plus one per
+    # (sequence, KV head); each slot holds Hq / Hkv partials of (d_h + 2) fp32; then
+    # num_seqs + 1 int32 block offsets
+    assert e.attn_decode_workspace_bytes(64, 32, 8, 128, 512, 16) == (2048 + 64 * 8) * 4 * 130 * 4 + 65 * 4
+    assert e.attn_decode_workspace_bytes(1, 1, 1, 128, 1, 16) == 2 * 130 * 4 + 2 * 4
+    assert e.attn_decode_workspace_bytes(2, 8, 2, 128, 3, 16) == (12 + 4) * 4 * 130 * 4 + 3 * 4
+    assert e.attn_decode_workspace_bytes(0, 32, 8, 128, 512, 16) == 0
+    assert e.attn_decode_workspace_bytes(4, 32, 6, 128, 512, 16) == 0
 
 
 def test_gather_validation(lib):

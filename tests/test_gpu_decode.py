@@ -53,6 +53,31 @@ def test_decode_full_workload():
     check_close(f64(out), ro, "bf16", "decode64", f64(lse), rl)
 
 
+def test_decode_long_runs():
+    """Enough work that each wave's run spans more than 128 cache blocks (several 64-entry
+    block-table windows per piece); checked on a sample of sequences (their blocks copied
+    out into a compact cache for the oracle)."""
+    from exact_transformer_attention_amd import attn_decode_paged
+    cfg = workloads.scaled(workloads.CONFIGS["decode64"], num_seqs=32, len_lo=22000, len_hi=26000, seed=11)
+    d = workloads.make_decode_inputs(**cfg, device="cuda")
+    total = int(sum((int(L) + 15) // 16 for L in d["seq_lens"].tolist())) * cfg["Hkv"]
+    say(f"decode long runs: {total} (sequence, KV head, block) triples")
+    assert total // 2048 > 128
+    bt, sl = d["block_table"], d["seq_lens"]
+    out, lse = attn_decode_paged(d["q"], d["k_cache"], d["v_cache"], bt.cuda(), sl.cuda(), block_size=16,
+                                 rope_base=cfg["rope_base"])
+    torch.cuda.synchronize()
+    for b in (0, 7, 19, 31):
+        n = (int(sl[b]) + 15) // 16
+        ids = bt[b, :n].long()
+        kc = d["k_cache"][ids.cuda()].cpu()
+        vc = d["v_cache"][ids.cuda()].cpu()
+        tb = torch.arange(n, dtype=torch.int32)[None]
+        ro, rl = oracle.decode_paged(f64(d["q"][b:b + 1].cpu()), f64(kc), f64(vc), tb.numpy(), sl[b:b + 1].numpy(), 16,
+                                     rope_base=cfg["rope_base"])
+        check_close(f64(out[b:b + 1].cpu()), ro, "bf16", f"long runs seq {b}", f64(lse[b:b + 1].cpu()), rl)
+
+
 def test_gather_bit_exact():
     """The block-table address code, copied out by attn_paged_gather, equals the oracle's
     gather bit for bit (both dtypes)."""

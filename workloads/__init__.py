@@ -61,7 +61,7 @@ def make_fwd_inputs(B, Hq, Hkv, T, S, d_h, dtype="bf16", sigma=1.0, seed=0, **_)
 
 
 def make_decode_inputs(num_seqs, Hq, Hkv, d_h, block_size=16, len_lo=512, len_hi=8192,
-                       dtype="bf16", sigma=1.0, seed=0, seq_lens=None, **_):
+                       dtype="bf16", sigma=1.0, seed=0, seq_lens=None, device=None, **_):
     """Paged KV cache for one decode step.
 
     Draw order: seq_lens = randint(len_lo, len_hi + 1) (inclusive range) unless given;
@@ -69,7 +69,9 @@ def make_decode_inputs(num_seqs, Hq, Hkv, d_h, block_size=16, len_lo=512, len_hi
     owns perm[off_b : off_b + ceil(L_b / block_size)] in order; unused table entries
     are -1.  Then q [num_seqs,Hq,d_h], k_cache and v_cache [N,Hkv,block_size,d_h]
     iid N(0, sigma^2), rounded to dtype.  Every slot of the pool is drawn, including
-    the slots past each sequence's length in its last block.
+    the slots past each sequence's length in its last block.  With `device` given, q and
+    the caches are drawn there by a generator of that device seeded with seed + 1
+    (for caches too large to draw on the host); lengths and tables stay host-drawn.
     """
     g = torch.Generator("cpu").manual_seed(int(seed))
     td = _TORCH_DTYPE[dtype]
@@ -86,11 +88,15 @@ def make_decode_inputs(num_seqs, Hq, Hkv, d_h, block_size=16, len_lo=512, len_hi
     for b, n in enumerate(nblk):
         block_table[b, :n] = perm[off:off + n].to(torch.int32)
         off += n
-    q = (torch.randn((num_seqs, Hq, d_h), generator=g, dtype=torch.float32) * sigma).to(td)
+    kw = {}
+    if device is not None:
+        g = torch.Generator(device).manual_seed(int(seed) + 1)
+        kw = dict(device=device)
+    q = (torch.randn((num_seqs, Hq, d_h), generator=g, dtype=torch.float32, **kw) * sigma).to(td)
     k_cache = (torch.randn((num_blocks, Hkv, block_size, d_h), generator=g,
-                           dtype=torch.float32) * sigma).to(td)
+                           dtype=torch.float32, **kw) * sigma).to(td)
     v_cache = (torch.randn((num_blocks, Hkv, block_size, d_h), generator=g,
-                           dtype=torch.float32) * sigma).to(td)
+                           dtype=torch.float32, **kw) * sigma).to(td)
     return dict(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
                 seq_lens=seq_lens.to(torch.int32), block_size=block_size,
                 num_blocks=num_blocks, max_blocks_per_seq=block_table.shape[1])
