@@ -42,6 +42,31 @@ __device__ __forceinline__ void load_lds16(const void* gptr, void* lds_wave_base
 #endif
 }
 
+// Buffer resource (V#) of a raw byte range: reads at offsets >= bytes return zero.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);  // stride 0
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;  // raw 32-bit data, no swizzle
+  return r;
+}
+
+__device__ void llvm_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size,
+                                         int voffset, int soffset, int offset,
+                                         int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// 16 bytes at byte offset voffset of a buffer straight into LDS (buffer_load_dwordx4 ...
+// lds): lane i writes lds_wave_base + 16 * i.  The resource and LDS base are
+// wave-uniform, so the per-lane address costs no vector arithmetic.
+__device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, int voffset, void* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  llvm_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voffset, 0, 0, 0);
+#endif
+}
+
 // sin and cos of 2*pi*rev for |rev| <= 0.5 (hardware v_sin/v_cos take revolutions).
 __device__ __forceinline__ void sincos_rev(float rev, float* s, float* c) {
   *s = __builtin_amdgcn_sinf(rev);

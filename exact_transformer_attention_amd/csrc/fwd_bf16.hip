@@ -201,23 +201,30 @@ void fwd_bf16_kernel(FwdParams p) {
   }
 
   // Direct-to-LDS loads: raw K of block `tile` into Kraw[tile & 1] (two blocks ahead of
-  // its use), V of block `tile` into Vs[tile & 1] (one block ahead).  NCH loads each.
-  auto load_k = [&](int tile) {
-    const int k0 = tile * kBN;
+  // its use), V of block `tile` into Vs[tile & 1] (one block ahead).  NCH loads each,
+  // through a buffer resource starting at the block's first row: the per-lane offsets
+  // are fixed, and rows past S read as zero (they are never visible).
+  int koff[C::NCH], voff[C::NCH];
 #pragma unroll
-    for (int j = 0; j < C::NCH; ++j) {
-      const int s = min(k0 + row0 + j * C::RSTEP, S - 1);  // rows past S are never visible
-      load_lds16(kg + (size_t)s * D + slot * 8, &Kraw[tile & 1][(wid * C::NCH + j) * kWave]);
-    }
+  for (int j = 0; j < C::NCH; ++j) {
+    const int r = row0 + j * C::RSTEP;
+    koff[j] = (r * D + slot * 8) * 2;
+    voff[j] = (r * D + (slot ^ vswz<D>(r)) * 8) * 2;
+  }
+  auto block_rsrc = [&](const __bf16* base, int k0) {
+    return make_rsrc(base + (size_t)k0 * D, (uint32_t)(S - k0) * D * 2);
+  };
+  auto load_k = [&](int tile) {
+    const i32x4 rs = block_rsrc(kg, tile * kBN);
+#pragma unroll
+    for (int j = 0; j < C::NCH; ++j)
+      buffer_load_lds16(rs, koff[j], &Kraw[tile & 1][(wid * C::NCH + j) * kWave]);
   };
   auto load_v = [&](int tile) {
-    const int k0 = tile * kBN;
+    const i32x4 rs = block_rsrc(vg, tile * kBN);
 #pragma unroll
-    for (int j = 0; j < C::NCH; ++j) {
-      const int r = row0 + j * C::RSTEP;
-      const int s = min(k0 + r, S - 1);
-      load_lds16(vg + (size_t)s * D + (slot ^ vswz<D>(r)) * 8, &Vs[tile & 1][(wid * C::NCH + j) * kWave]);
-    }
+    for (int j = 0; j < C::NCH; ++j)
+      buffer_load_lds16(rs, voff[j], &Vs[tile & 1][(wid * C::NCH + j) * kWave]);
   };
   // Rotate this thread's raw K chunks of block `tile` into Ks[tile & 1].  The caller has
   // waited for the loads of that block.
