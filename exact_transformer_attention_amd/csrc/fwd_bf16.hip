@@ -316,6 +316,69 @@ void fwd_bf16_kernel(FwdParams p) {
       }
     }
   };
+  // The same product with the rotation of the next K block woven in: after each k-step
+  // (its MFMAs issued), one unit of the rotation (one 4-pair slice of one of this
+  // thread's chunks).  The scheduling barrier after each slice keeps the order, so the
+  // rotation's vector instructions run while the matrix cores work on that k-step
+  // (the K chunks this thread rotates per block, D / 64 of them with 4 pairs each, make
+  // exactly D / 16 units, one per k-step).
+  auto qk_rot = [&](const __bf16* kb, f32x16 (&s)[2][kNB], auto kbc) {
+    constexpr int kn = decltype(kbc)::value;  // buffer of the block being rotated
+    static_assert(C::NCH * 4 == C::KS, "one rotation unit per k-step");
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
+        const bf16x8 bop = __builtin_bit_cast(
+            bf16x8, (u32x4){g == 0 ? (__builtin_bit_cast(uint32_t, -bias) >> 16) : 0u, 0u, 0u, 0u});
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_op, bop, acc, 0, 0, 0);
+      }
+    u32x4 raw[C::NCH], out[C::NCH];
+#pragma unroll
+    for (int j = 0; j < C::NCH; ++j) raw[j] = Kraw[kn][(wid * C::NCH + j) * kWave + lane];
+    float c[4], sn[4];
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[e] = ac[e];
+        sn[e] = as[e];
+      }
+    }
+    bf16x8 a[C::KS][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) a[ks][mb] = *(const bf16x8*)(kb + (mb * 32 + l32) * C::KSTR + ks * 16 + g * 8);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      if (ks + 2 < C::KS) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          a[ks + 2][mb] = *(const bf16x8*)(kb + (mb * 32 + l32) * C::KSTR + (ks + 2) * 16 + g * 8);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+          s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][mb], qop[nb][ks], s[mb][nb], 0, 0, 0);
+      // rotation unit ks: pair slot e of chunk j
+      const int j = ks / 4, e = ks % 4;
+      if constexpr (ROPE) {
+        const float x0 = bf16_lo(raw[j][e]), x1 = bf16_hi(raw[j][e]);
+        out[j][e] = pack_bf16(x0 * c[e] - x1 * sn[e], x0 * sn[e] + x1 * c[e]);
+        if (j + 1 < C::NCH) cmul(c[e], sn[e], rc[e], rs[e]);
+        else cmul(ac[e], as[e], tc[e], ts[e]);
+      } else {
+        out[j][e] = raw[j][e];
+      }
+      if (e == 3) *(u32x4*)&Ks[kn][(row0 + j * C::RSTEP) * C::KSTR + slot * 8] = out[j];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   // exp2 of one 32-key half for both n-blocks -> bf16 P operands and this half's row sums.
   auto expo = [&](f32x16 (&s)[2][kNB], int mb, bf16x8 (&pop)[kNB][4], float (&lt)[kNB]) {
 #pragma unroll
@@ -381,8 +444,9 @@ void fwd_bf16_kernel(FwdParams p) {
     const char* vbuf = (const char*)&Vs[PAR][0];
     if (k0 < nk_wave) {
       f32x16 s[2][kNB];
-      qk(kbuf, s);
-      if (rot) rotate_k(it + 1, std::integral_constant<int, PAR ^ 1>{});
+      // The rotation of block it+1 is woven into the product; after the last block it
+      // rotates stale data into a buffer nobody reads.
+      qk_rot(kbuf, s, std::integral_constant<int, PAR ^ 1>{});
       // mask (diagonal / tail blocks only)
       const bool need_mask = (k0 + kBN > S) || (p.causal && (int64_t)(k0 + kBN - 1) > pos + wrow0);
       if (need_mask) {
