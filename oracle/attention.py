@@ -111,6 +111,18 @@ def causal_mask(q_positions, k_positions):
     return np.where(kp <= qp, 0.0, -np.inf).astype(F64)
 
 
+def window_mask(q_positions, k_positions, window):
+    """Additive causal sliding-window mask: 0 where q - window < k <= q, -inf elsewhere.
+
+    Each query sees the `window` most recent positions up to and including its own
+    ("22 interview questions on attention & transformers", What is sparse /
+    sliding-window attention: a fixed neighbourhood of size w, read here as the causal
+    window of the sliding-window decoders that section names)."""
+    qp = np.asarray(q_positions, dtype=np.int64)[:, None]
+    kp = np.asarray(k_positions, dtype=np.int64)[None, :]
+    return np.where((kp <= qp) & (kp > qp - int(window)), 0.0, -np.inf).astype(F64)
+
+
 def kv_head_of(h, Hq, Hkv):
     """Contiguous grouped-query map: query head h reads KV head h // (Hq / Hkv)."""
     return h // (Hq // Hkv)
@@ -118,14 +130,21 @@ def kv_head_of(h, Hq, Hkv):
 
 # ------------------------------------------------------------ prefill ----
 
-def attention(q, k, v, causal=False, rope_base=0.0, pos=0, row_block=None, return_probs=False):
+def _mask(qpos, kpos, causal, window):
+    if window:
+        return window_mask(qpos, kpos, window)
+    return causal_mask(qpos, kpos) if causal else None
+
+
+def attention(q, k, v, causal=False, rope_base=0.0, pos=0, row_block=None, return_probs=False, window=0):
     """Exact attention over whole tensors.
 
     q [B,Hq,T,d_h], k and v [B,Hkv,S,d_h] (any float dtype; used as float64).
     RoPE (if rope_base > 0) rotates query row t at position pos + t and key s
     at position s; V is not rotated.  If causal, key s is visible to query t
-    iff s <= pos + t.  Returns (out [B,Hq,T,d_h], lse [B,Hq,T]) in float64, and
-    also the probabilities [B,Hq,T,S] if return_probs.
+    iff s <= pos + t; with window = w > 0 (causal sliding window) iff
+    pos + t - w < s <= pos + t.  Returns (out [B,Hq,T,d_h], lse [B,Hq,T]) in
+    float64, and also the probabilities [B,Hq,T,S] if return_probs.
 
     row_block bounds memory for long sequences: each (b, h) is processed in
     slices of row_block query rows, every row still getting its full
@@ -150,7 +169,7 @@ def attention(q, k, v, causal=False, rope_base=0.0, pos=0, row_block=None, retur
             for t0 in range(0, T, rb):
                 t1 = min(T, t0 + rb)
                 qr = apply_rope(q[b, h, t0:t1], qpos[t0:t1], rope_base)
-                mask = causal_mask(qpos[t0:t1], kpos) if causal else None
+                mask = _mask(qpos[t0:t1], kpos, causal, window)
                 o, l, p = sdpa(qr, kr[b, g], v[b, g], mask)
                 out[b, h, t0:t1] = o
                 lse[b, h, t0:t1] = l
@@ -161,7 +180,7 @@ def attention(q, k, v, causal=False, rope_base=0.0, pos=0, row_block=None, retur
     return out, lse
 
 
-def attention_rows(q, k, v, rows, causal=False, rope_base=0.0, pos=0):
+def attention_rows(q, k, v, rows, causal=False, rope_base=0.0, pos=0, window=0):
     """The same definition evaluated only at selected query rows.
 
     rows: int array [n, 3] of (b, h, t).  Each row is rotated at position
@@ -186,7 +205,7 @@ def attention_rows(q, k, v, rows, causal=False, rope_base=0.0, pos=0):
         kr = cache[key]
         p = pos + int(t)
         qr = apply_rope(q[b, h, t:t + 1].astype(F64), np.array([p]), rope_base)
-        mask = causal_mask(np.array([p]), kpos) if causal else None
+        mask = _mask(np.array([p]), kpos, causal, window)
         o, l, _ = sdpa(qr, kr, v[b, g].astype(F64), mask)
         out[i] = o[0]
         lse[i] = l[0]

@@ -38,8 +38,9 @@ def _bf_rotate(vec, p, base):
     return out
 
 
-def brute_force_attention(q, k, v, causal, base, pos):
-    """q: nested lists [B][Hq][T][d]; k, v: [B][Hkv][S][d].  Returns (out, lse) as lists."""
+def brute_force_attention(q, k, v, causal, base, pos, window=0):
+    """q: nested lists [B][Hq][T][d]; k, v: [B][Hkv][S][d].  Returns (out, lse) as lists.
+    window > 0: causal sliding window, key s visible iff pos + t - window < s <= pos + t."""
     B, Hq, T, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
     Hkv, S = len(k[0]), len(k[0][0])
     group = Hq // Hkv
@@ -52,7 +53,10 @@ def brute_force_attention(q, k, v, causal, base, pos):
                 qt = _bf_rotate(q[b][h][t], pos + t, base)
                 logits = []
                 for s in range(S):
-                    if causal and s > pos + t:
+                    if (causal or window) and s > pos + t:
+                        logits.append(None)
+                        continue
+                    if window and s <= pos + t - window:
                         logits.append(None)
                         continue
                     ks = _bf_rotate(k[b][g][s], s, base)
@@ -97,6 +101,65 @@ def check_bruteforce_tiny(orc, n_cases=40):
         fin = np.isfinite(bl)
         assert np.array_equal(fin, np.isfinite(l))
         assert np.allclose(l[fin], bl[fin], rtol=0, atol=1e-12), case
+
+
+def check_bruteforce_window(orc, n_cases=30):
+    """Causal sliding window against the scalar brute force, windows from 1 to past T."""
+    rng = _rng(11)
+    for case in range(n_cases):
+        T = int(rng.integers(1, 9))
+        S = int(rng.integers(1, 9))
+        Hq, Hkv = [(1, 1), (4, 2), (2, 1)][case % 3]
+        d = [2, 4, 8][int(rng.integers(0, 3))]
+        base = [0.0, 10000.0][case % 2]
+        pos = [0, 2, 5][case % 3]
+        w = int(rng.integers(1, 11))
+        q = rng.standard_normal((1, Hq, T, d))
+        k = rng.standard_normal((1, Hkv, S, d))
+        v = rng.standard_normal((1, Hkv, S, d))
+        o, l = orc.attention(q, k, v, causal=True, rope_base=base, pos=pos, window=w)
+        bo, bl = brute_force_attention(q.tolist(), k.tolist(), v.tolist(), True, base, pos, window=w)
+        bo = np.array(bo, dtype=np.float64)
+        bl = np.array(bl, dtype=np.float64)
+        assert np.allclose(o, bo, rtol=0, atol=1e-12), (case, np.max(np.abs(o - bo)))
+        fin = np.isfinite(bl)
+        assert np.array_equal(fin, np.isfinite(l)), case
+        assert np.allclose(l[fin], bl[fin], rtol=0, atol=1e-12), case
+
+
+def check_window_special_cases(orc):
+    """A window reaching back past key 0 is plain causal attention; a window of 1 leaves
+    each query its own key only (O_t = v at pos + t, lse = that logit); with Q = 0 the
+    output is the mean of the values in the window."""
+    rng = _rng(12)
+    Hq, Hkv, T, S, d, pos = 4, 2, 9, 12, 8, 3
+    q = rng.standard_normal((1, Hq, T, d))
+    k = rng.standard_normal((1, Hkv, S, d))
+    v = rng.standard_normal((1, Hkv, S, d))
+    oc, lc = orc.attention(q, k, v, causal=True, rope_base=10000.0, pos=pos)
+    for w in (pos + T, pos + T + 5, 10 ** 6):
+        ow, lw = orc.attention(q, k, v, causal=True, rope_base=10000.0, pos=pos, window=w)
+        assert np.array_equal(ow, oc) and np.array_equal(lw, lc), w
+    o1, l1 = orc.attention(q, k, v, causal=True, rope_base=0.0, pos=pos, window=1)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        for t in range(T):
+            s_ = pos + t
+            if s_ < S:
+                assert np.allclose(o1[0, h, t], v[0, g, s_], atol=1e-14)
+                assert abs(l1[0, h, t] - float(q[0, h, t] @ k[0, g, s_]) / math.sqrt(d)) < 1e-12
+            else:
+                assert not np.isfinite(l1[0, h, t]) and np.all(o1[0, h, t] == 0)
+    for w in (2, 5):
+        o0, l0 = orc.attention(np.zeros_like(q), k, v, causal=True, rope_base=10000.0, pos=pos, window=w)
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            for t in range(T):
+                lo, hi = max(0, pos + t - w + 1), min(S, pos + t + 1)
+                if hi <= lo:
+                    continue
+                assert np.allclose(o0[0, h, t], v[0, g, lo:hi].mean(axis=0), atol=1e-13)
+                assert abs(l0[0, h, t] - math.log(hi - lo)) < 1e-13
 
 
 # ------------------------------------------------------------------------
@@ -430,6 +493,8 @@ def check_cross_attention_shapes(orc):
 
 
 ALL_CHECKS = [
+    check_bruteforce_window,
+    check_window_special_cases,
     check_bruteforce_tiny, check_q_zero_gives_mean, check_single_key, check_causal_first_row,
     check_one_hot_logit_closed_form, check_rope_d2_is_plane_rotation, check_rope_d4_frequencies,
     check_rope_identity_at_zero, check_rope_relative_and_norm, check_rows_sum_to_one,

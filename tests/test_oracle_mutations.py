@@ -82,7 +82,7 @@ def m_rope_rotate_half_pairs(mod):
 def m_rope_only_queries(mod):
     orig_attention = mod.attention
 
-    def attention(q, k, v, causal=False, rope_base=0.0, pos=0, row_block=None, return_probs=False):
+    def attention(q, k, v, causal=False, rope_base=0.0, pos=0, row_block=None, return_probs=False, window=0):
         real = mod.apply_rope
         calls = {"n": 0}
 
@@ -91,7 +91,7 @@ def m_rope_only_queries(mod):
             return real(x, p, 0.0) if calls["n"] == 1 else real(x, p, base)
         mod.apply_rope = rope_skip_first
         try:
-            return orig_attention(q, k, v, causal, rope_base, pos, row_block, return_probs)
+            return orig_attention(q, k, v, causal, rope_base, pos, row_block, return_probs, window)
         finally:
             mod.apply_rope = real
     mod.attention = attention
@@ -126,8 +126,8 @@ def m_lse_without_max(mod):
 def m_pos_ignored(mod):
     orig = mod.attention
 
-    def attention(q, k, v, causal=False, rope_base=0.0, pos=0, row_block=None, return_probs=False):
-        return orig(q, k, v, causal, rope_base, 0, row_block, return_probs)
+    def attention(q, k, v, causal=False, rope_base=0.0, pos=0, row_block=None, return_probs=False, window=0):
+        return orig(q, k, v, causal, rope_base, 0, row_block, return_probs, window)
     mod.attention = attention
 
 
@@ -189,7 +189,16 @@ def m_no_max_subtraction_overflow(mod):
     mod.sdpa = sdpa
 
 
-MUTATIONS = [m_mask_after_softmax, m_no_scale, m_scale_by_d, m_rope_freq_exponent, m_rope_clockwise,
+def m_window_off_by_one(mod):
+    """The window keeps one key too many (s >= q - w instead of s > q - w)."""
+    def window_mask(qp, kp, window):
+        qp = np.asarray(qp, dtype=np.int64)[:, None]
+        kp = np.asarray(kp, dtype=np.int64)[None, :]
+        return np.where((kp <= qp) & (kp >= qp - int(window)), 0.0, -np.inf)
+    mod.window_mask = window_mask
+
+
+MUTATIONS = [m_window_off_by_one, m_mask_after_softmax, m_no_scale, m_scale_by_d, m_rope_freq_exponent, m_rope_clockwise,
              m_rope_rotate_half_pairs, m_rope_only_queries, m_gqa_modulo, m_causal_off_by_one,
              m_lse_without_max, m_pos_ignored, m_decode_position_L, m_gather_swapped,
              m_probs_transposed, m_no_max_subtraction_overflow]
