@@ -55,7 +55,7 @@ def measured_traffic(kind, digest):
     return t.get("hbm_bytes_per_launch")
 
 
-def summarize_pmc(fetch_csv, write_csv, out_dir):
+def summarize_pmc(fetch_csv, write_csv, out_dir, window_run=False):
     """Per-launch HBM traffic of the timed kernels from two rocprofv3 --pmc runs (FETCH_SIZE,
     then WRITE_SIZE; kilobytes per dispatch), scaled by the factor the same counters read
     for a plain 1 GiB device copy (run with --copy-calibration).  Writes
@@ -97,8 +97,16 @@ def summarize_pmc(fetch_csv, write_csv, out_dir):
     w_scale = copy_bytes / w_copy if w_copy else 1.0
     res = {"calibration": {"kernel": "1 GiB device copy", "fetch_raw_bytes": f_copy, "write_raw_bytes": w_copy,
                            "fetch_scale": f_scale, "write_scale": w_scale}}
-    for kind, keys, srcs in (("prefill", ["fwd_bf16_kernel"], PREFILL_SOURCES),
-                             ("decode", ["decode_partial_kernel", "decode_merge_kernel"], DECODE_SOURCES)):
+    kinds = ((("window", ["fwd_bf16_kernel"], PREFILL_SOURCES),) if window_run else
+             (("prefill", ["fwd_bf16_kernel"], PREFILL_SOURCES),
+              ("decode", ["decode_partial_kernel", "decode_merge_kernel"], DECODE_SOURCES)))
+    path = os.path.join(out_dir, "traffic.json")
+    if window_run and os.path.exists(path):  # a window run adds its entry to the main one
+        with open(path) as f:
+            old = json.load(f)
+        old["window_calibration"] = res["calibration"]
+        res = old
+    for kind, keys, srcs in kinds:
         fb = [pick(fetch, k) for k in keys]
         wb = [pick(write, k) for k in keys]
         if any(x is None for x in fb + wb):
@@ -108,7 +116,7 @@ def summarize_pmc(fetch_csv, write_csv, out_dir):
         res[kind] = {"kernels": keys, "fetch_bytes_per_launch": rd, "write_bytes_per_launch": wr,
                      "hbm_bytes_per_launch": rd + wr, "source_digest": kernel_sources_digest(srcs)}
     os.makedirs(out_dir, exist_ok=True)
-    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+    with open(path, "w") as f:
         json.dump(res, f, indent=1)
     return res
 
@@ -159,6 +167,78 @@ def cpu_baseline_decode(d, cfg, n_seqs=64):
                 sample=f"first {n_seqs} of {cfg['num_seqs']} sequences ({int(sl.sum())} tokens), fp64 numpy")
 
 
+def cpu_baseline_window(cfg, window, n_kv=2):
+    """The fp64 oracle on a bounded sample of the window workload: batch 0, the query heads of
+    the first n_kv KV heads, all rows (the oracle materialises the full masked score matrix)."""
+    import oracle
+    import workloads
+    q, k, v = workloads.make_fwd_inputs(**cfg)
+    nq = n_kv * (cfg["Hq"] // cfg["Hkv"])
+    qs, ks, vs = q[:1, :nq].double().numpy(), k[:1, :n_kv].double().numpy(), v[:1, :n_kv].double().numpy()
+    t0 = time.perf_counter()
+    oracle.attention(qs, ks, vs, causal=True, rope_base=cfg["rope_base"], pos=cfg["pos"], row_block=1024,
+                     window=window)
+    dt = time.perf_counter() - t0
+    flops = workloads.window_flops(1, nq, cfg["T"], cfg["S"], cfg["d_h"], window, cfg["pos"])
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cpu_threads(), kind="oracle", seconds=round(dt, 3),
+                sample=f"batch 0, query heads 0-{nq - 1} (KV heads 0-{n_kv - 1}), all {cfg['T']} rows, fp64 numpy, "
+                       f"1024-row blocks; {flops:.3e} algorithmic FLOP")
+
+
+def window_bench(a):
+    """Causal sliding-window prefill on the 8192-token GQA workload (one JSON line)."""
+    import torch
+    import workloads
+    from exact_transformer_attention_amd import attn_fwd_window
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS["gqa8k"]
+    w = a.window
+    q, k, v = (t.to(dev) for t in workloads.make_fwd_inputs(**cfg))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def run():
+        attn_fwd_window(q, k, v, w, rope_base=cfg["rope_base"], pos=cfg["pos"], out=out, lse=lse)
+
+    for _ in range(a.warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    avg = sum(ms) / len(ms)
+    assert bool(torch.isfinite(out).all())
+    if a.copy_calibration:
+        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+    flops = workloads.window_flops(cfg["B"], cfg["Hq"], cfg["T"], cfg["S"], cfg["d_h"], w, cfg["pos"])
+    tf = flops / (avg * 1e-3) / 1e12
+    res = {
+        "metric": "sliding-window attention fwd TFLOP/s + % bf16 MFMA peak",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(avg, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded iid normal, bf16-rounded)",
+        "config": {"workload": f"causal sliding-window GQA prefill B=2 Hq=32 Hkv=8 T=S=8192 d_h=128 RoPE 1e4, "
+                               f"window {w}", "window": w},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("window", kernel_sources_digest(PREFILL_SOURCES)),
+                     "kernel": "fwd_bf16_kernel<128,4>", "flop_per_launch": flops, "avg_launch_ms": round(avg, 4)},
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the oracle on the host (window sample)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_window(cfg, w)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,19 +247,26 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="time only one part (profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "window"], default=None,
+                    help="time only one part (profiling runs); 'window' times the causal sliding-window "
+                         "prefill (attn_fwd_window) on the same 8192-token GQA workload instead")
+    ap.add_argument("--window", type=int, default=4096, help="window of --only window (keys)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
-                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/traffic.json")
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/traffic.json "
+                         "(with --only window: CSVs of a window run, added as the 'window' entry)")
     a = ap.parse_args()
     if a.traffic_from:
-        print(json.dumps(summarize_pmc(a.traffic_from[0], a.traffic_from[1], os.path.join(ROOT, "profiles")),
-                         indent=1))
+        print(json.dumps(summarize_pmc(a.traffic_from[0], a.traffic_from[1], os.path.join(ROOT, "profiles"),
+                                       window_run=a.only == "window"), indent=1))
         return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the kernels are "
               "single-GPU and no multi-GPU path is built.", file=sys.stderr)
         sys.exit(2)
+
+    if a.only == "window":
+        window_bench(a)
+        return
 
     import torch
     import workloads

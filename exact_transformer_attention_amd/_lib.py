@@ -15,8 +15,8 @@ LIB_PATH = os.path.join(PKG, "libattn.so")
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
 ATTN_F32, ATTN_BF16 = 0, 1
 
-EXPORTED = ("attn_fwd", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_paged_gather",
-            "attn_status_str")
+EXPORTED = ("attn_fwd", "attn_fwd_window", "attn_decode_paged", "attn_decode_workspace_bytes",
+            "attn_paged_gather", "attn_status_str")
 
 
 def _load():
@@ -27,6 +27,8 @@ def _load():
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i64, i32, vp]
     lib.attn_fwd.restype = i32
+    lib.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, f32, i64, i32, vp]
+    lib.attn_fwd_window.restype = i32
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp,
                                       vp, sz, i32, vp]
     lib.attn_decode_paged.restype = i32
@@ -81,11 +83,7 @@ def _require(cond, msg):
         raise ValueError(msg)
 
 
-def attn_fwd(q, k, v, causal=False, rope_base=0.0, pos=0, out=None, lse=None, want_lse=True,
-             stream=None):
-    """Exact attention.  q [B,Hq,T,d_h], k/v [B,Hkv,S,d_h] contiguous device tensors of one
-    dtype (bf16 or fp32).  Returns (out, lse) with out like q and lse fp32 [B,Hq,T]
-    (None if want_lse is False and no lse buffer was given)."""
+def _fwd_buffers(q, k, v, out, lse, want_lse):
     import torch
     _require(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D")
     B, Hq, T, d = q.shape
@@ -101,9 +99,28 @@ def attn_fwd(q, k, v, causal=False, rope_base=0.0, pos=0, out=None, lse=None, wa
     _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "bad out")
     if lse is not None:
         _require(lse.shape == (B, Hq, T) and lse.dtype == torch.float32 and lse.is_contiguous(), "bad lse")
+    return out, lse, (B, Hq, Hkv, T, S, d)
+
+
+def attn_fwd(q, k, v, causal=False, rope_base=0.0, pos=0, out=None, lse=None, want_lse=True,
+             stream=None):
+    """Exact attention.  q [B,Hq,T,d_h], k/v [B,Hkv,S,d_h] contiguous device tensors of one
+    dtype (bf16 or fp32).  Returns (out, lse) with out like q and lse fp32 [B,Hq,T]
+    (None if want_lse is False and no lse buffer was given)."""
+    out, lse, (B, Hq, Hkv, T, S, d) = _fwd_buffers(q, k, v, out, lse, want_lse)
     st = LIB.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, T, S, d,
                       int(bool(causal)), float(rope_base), int(pos), _dtype_code(q), _stream(stream))
     _check(st, "attn_fwd")
+    return out, lse
+
+
+def attn_fwd_window(q, k, v, window, rope_base=0.0, pos=0, out=None, lse=None, want_lse=True, stream=None):
+    """Causal sliding-window attention: query row t sees keys pos + t - window < s <= pos + t.
+    Same tensors and results as attn_fwd."""
+    out, lse, (B, Hq, Hkv, T, S, d) = _fwd_buffers(q, k, v, out, lse, want_lse)
+    st = LIB.attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, T, S, d,
+                             int(window), float(rope_base), int(pos), _dtype_code(q), _stream(stream))
+    _check(st, "attn_fwd_window")
     return out, lse
 
 

@@ -38,8 +38,12 @@ const char* attn_status_str(attn_status_t s) {
   return "unknown status";
 }
 
-attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
-                       int Hkv, int T, int S, int d_h, int causal, float rope_base, int64_t pos,
+}  // extern "C"
+
+namespace {
+
+attn_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
+                       int T, int S, int d_h, int causal, int64_t window, float rope_base, int64_t pos,
                        attn_dtype_t dtype, void* stream) {
   if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || d_h < 1) return ATTN_ERR_INVALID_ARG;
@@ -63,6 +67,7 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
   p.T = T;
   p.S = S;
   p.causal = causal;
+  p.window = window;
   p.pos = pos;
   p.use_rope = rope_base > 0.f;
   fill_rope(p.rope_c, d_h, p.use_rope ? rope_base : 1.f);
@@ -70,6 +75,24 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = (dtype == ATTN_F32) ? attn::launch_fwd_f32(p, d_h, st) : attn::launch_fwd_bf16(p, d_h, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+                       int Hkv, int T, int S, int d_h, int causal, float rope_base, int64_t pos,
+                       attn_dtype_t dtype, void* stream) {
+  return fwd_impl(q, k, v, out, lse, B, Hq, Hkv, T, S, d_h, causal, 0, rope_base, pos, dtype, stream);
+}
+
+attn_status_t attn_fwd_window(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                              int Hq, int Hkv, int T, int S, int d_h, int64_t window, float rope_base,
+                              int64_t pos, attn_dtype_t dtype, void* stream) {
+  if (window < 1) return ATTN_ERR_INVALID_ARG;
+  if (window > ((int64_t)1 << 41)) window = (int64_t)1 << 41;  // wider than any reach: plain causal
+  return fwd_impl(q, k, v, out, lse, B, Hq, Hkv, T, S, d_h, 1, window, rope_base, pos, dtype, stream);
 }
 
 size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_h, int max_blocks_per_seq,

@@ -149,6 +149,14 @@ void fwd_bf16_kernel(FwdParams p) {
     nk_wg = (int)(lg < 0 ? 0 : (lg < S ? lg : S));
   }
   const int n_tiles = (nk_wg + kBN - 1) / kBN;
+  // Sliding window: the first key visible to the wave's / the workgroup's first row.
+  int64_t lo_wave = 0;
+  int it0 = 0;
+  if (p.window > 0) {
+    lo_wave = pos + wrow0 - p.window + 1;
+    const int64_t lo_wg = pos + (int64_t)qb * RH - p.window + 1;
+    it0 = (int)(lo_wg <= 0 ? 0 : (lo_wg < nk_wg ? lo_wg : nk_wg)) / kBN;
+  }
 
   // ---- Q^T operand in registers: lane holds query l32 of n-block nb, dims ks*16 + g*8.
   bf16x8 qop[kNB][C::KS];
@@ -260,9 +268,9 @@ void fwd_bf16_kernel(FwdParams p) {
   };
   // Exact angles of this thread's first key of block `tile` (every kResync blocks; the
   // angle addition in rotate_k advances them in between).
-  auto resync = [&](int tile) {
+  auto resync = [&](int tile, bool force = false) {
     if constexpr (ROPE) {
-      if (tile % kResync == 0) {
+      if (force || tile % kResync == 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           sincos_rev(rope_turns((int64_t)tile * kBN + row0, cturn[e]), &as[e], &ac[e]);
@@ -442,13 +450,14 @@ void fwd_bf16_kernel(FwdParams p) {
     const int k0 = it * kBN;
     const __bf16* kbuf = &Ks[PAR][0];
     const char* vbuf = (const char*)&Vs[PAR][0];
-    if (k0 < nk_wave) {
+    if (k0 < nk_wave && (int64_t)(k0 + kBN) > lo_wave) {
       f32x16 s[2][kNB];
       // The rotation of block it+1 is woven into the product; after the last block it
       // rotates stale data into a buffer nobody reads.
       qk_rot(kbuf, s, std::integral_constant<int, PAR ^ 1>{});
       // mask (diagonal / tail blocks only)
-      const bool need_mask = (k0 + kBN > S) || (p.causal && (int64_t)(k0 + kBN - 1) > pos + wrow0);
+      const bool need_mask = (k0 + kBN > S) || (p.causal && (int64_t)(k0 + kBN - 1) > pos + wrow0) ||
+                             (p.window > 0 && (int64_t)k0 < lo_wave + kQW - 1);
       if (need_mask) {
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
@@ -458,7 +467,8 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = k0 + mb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-              const bool vis = key < S && (!p.causal || (int64_t)key <= lim);
+              const bool vis = key < S && (!p.causal || (int64_t)key <= lim) &&
+                               (p.window <= 0 || (int64_t)key > lim - p.window);
               if (!vis) s[mb][nb][r] = -INFINITY;
             }
         }
@@ -516,16 +526,20 @@ void fwd_bf16_kernel(FwdParams p) {
     wait_loads();  // this thread's loads issued above have landed before the next barrier
   };
 
-  // ---- prologue: raw K of blocks 0 and 1 and V of block 0 in flight; block 0 rotated.
-  if (n_tiles > 0) {
-    load_k(0);
-    load_v(0);
-    if (n_tiles > 1) load_k(1);
+  // ---- prologue: raw K of the first two blocks and V of the first in flight; the first
+  // rotated.  The first block is 0, or the first one a sliding window reaches.
+  if (it0 < n_tiles) {
+    load_k(it0);
+    load_v(it0);
+    if (it0 + 1 < n_tiles) load_k(it0 + 1);
     wait_loads();
-    resync(0);
-    rotate_k(0, std::integral_constant<int, 0>{});
+    resync(it0, true);
+    if (it0 & 1) rotate_k(it0, std::integral_constant<int, 1>{});
+    else rotate_k(it0, std::integral_constant<int, 0>{});
   }
-  for (int it = 0; it < n_tiles; it += 2) {
+  int it = it0;
+  if (it < n_tiles && (it & 1)) step(std::integral_constant<int, 1>{}, it++);
+  for (; it < n_tiles; it += 2) {
     step(std::integral_constant<int, 0>{}, it);
     if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1);
   }

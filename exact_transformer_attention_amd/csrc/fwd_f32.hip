@@ -72,13 +72,19 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
     n_keys = (int)(last < 0 ? 0 : (last < S ? last : S));
   }
   const int64_t qpos = p.pos + t0 + row;
+  // Sliding window: keys below the window of the block's first row are never visible.
+  int k_first = 0;
+  if (p.window > 0) {
+    const int64_t lo = p.pos + t0 - p.window + 1;
+    k_first = (int)(lo <= 0 ? 0 : (lo < n_keys ? lo : n_keys)) / BN * BN;
+  }
 
   float m = -INFINITY, l = 0.f;
   float o[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) o[i] = 0.f;
 
-  for (int kt = 0; kt < n_keys; kt += BN) {
+  for (int kt = k_first; kt < n_keys; kt += BN) {
     __syncthreads();  // previous block's K/V/P no longer read
     for (int i = tid; i < BN * (D / 2); i += NT) {
       const int r = i / (D / 2), j = i % (D / 2);
@@ -115,7 +121,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
       float acc = 0.f;
 #pragma unroll 8
       for (int d = 0; d < D; ++d) acc = fmaf(Qs[row][d], Ks[kk][d], acc);
-      const bool vis = (s < S) && (!p.causal || (int64_t)s <= qpos);
+      const bool vis = (s < S) && (!p.causal || (int64_t)s <= qpos) && (p.window <= 0 || (int64_t)s > qpos - p.window);
       sc[i] = vis ? acc : -INFINITY;
       tmax = fmaxf(tmax, sc[i]);
     }

@@ -16,6 +16,7 @@ struct FwdParams {
   int B, Hq, Hkv, T, S;
   int causal;
   int use_rope;
+  int64_t window;  // > 0: causal sliding window, key s visible iff pos + t - window < s <= pos + t
   int n_qblocks;  // query blocks per (batch, head group)
   int n_groups;   // batch * head groups
   int xcd_remap;  // 1 if n_groups is a multiple of 8 (see work mapping in the kernel)

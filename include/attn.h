@@ -73,6 +73,23 @@ ATTN_API attn_status_t attn_fwd(const void* q, const void* k, const void* v, voi
                        float rope_base, int64_t pos, attn_dtype_t dtype, void* stream);
 
 /*
+ * attn_fwd_window -- causal sliding-window attention: key s is visible to query row t
+ * iff pos + t - window < s <= pos + t, i.e. each query sees the `window` most recent
+ * positions up to its own ("22 interview questions on attention & transformers", What
+ * is sparse / sliding-window attention: each token attends to a fixed neighbourhood of
+ * size w, cost O(n w); "Why is attention O(n^2) ...", Long context in practice: sliding
+ * window of width w, O(T w)).  Key blocks outside the window are not visited.
+ *
+ * Arguments, layouts, RoPE and the result are as for attn_fwd with causal = 1;
+ * window >= 1 (ATTN_ERR_INVALID_ARG otherwise), and a window reaching back past key 0
+ * gives exactly the causal result.
+ */
+ATTN_API attn_status_t attn_fwd_window(const void* q, const void* k, const void* v, void* out,
+                                       float* lse, int B, int Hq, int Hkv, int T, int S, int d_h,
+                                       int64_t window, float rope_base, int64_t pos,
+                                       attn_dtype_t dtype, void* stream);
+
+/*
  * attn_decode_paged -- one decode step over a block-tabled KV cache ("Self-Attention
  * Complexity, FlashAttention, PagedAttention, and RoPE in Code", Part 3: fixed-size
  * blocks and per-sequence block tables; "Why is attention O(n^2) ...": a decode step

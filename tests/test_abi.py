@@ -24,7 +24,7 @@ def lib():
 
 def test_header_declares_entry_points():
     names = header_functions()
-    assert names == sorted(["attn_fwd", "attn_decode_paged", "attn_decode_workspace_bytes",
+    assert names == sorted(["attn_fwd", "attn_fwd_window", "attn_decode_paged", "attn_decode_workspace_bytes",
                             "attn_paged_gather", "attn_status_str"])
 
 
@@ -66,6 +66,22 @@ def fwd(lib, **kw):
 ])
 def test_fwd_validation(lib, kw, status):
     assert fwd(lib, **kw) == status
+
+
+def fwd_window(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, B=1, Hq=4, Hkv=2, T=8, S=8, d=128, window=16,
+             base=10000.0, pos=0, dtype=1)
+    a.update(kw)
+    return lib.attn_fwd_window(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["T"],
+                               a["S"], a["d"], a["window"], a["base"], a["pos"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=0), 1), (dict(window=-3), 1), (dict(q=None), 1), (dict(Hq=6, Hkv=4), 1), (dict(dtype=9), 1),
+    (dict(d=96), 2), (dict(pos=1 << 41), 2),
+])
+def test_fwd_window_validation(lib, kw, status):
+    assert fwd_window(lib, **kw) == status
 
 
 def dec(lib, **kw):

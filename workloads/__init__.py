@@ -26,6 +26,7 @@ storage dtype with round-to-nearest-even (.to(torch.bfloat16)).
 """
 
 
+import numpy as np
 import torch
 
 # name -> parameters.  "seed" is fixed per workload.
@@ -108,6 +109,17 @@ def fwd_flops(B, Hq, T, S, d_h, causal, **_):
     return f / 2.0 if causal else f
 
 
+def window_flops(B, Hq, T, S, d_h, window, pos=0, **_):
+    """Algorithmic FLOPs of one causal sliding-window forward: 4*d_h per visible (query, key)
+    pair (QK^T and PV), counted exactly: query t sees keys max(0, pos+t-window+1) ..
+    min(S-1, pos+t)."""
+    t = np.arange(T, dtype=np.int64) + int(pos)
+    hi = np.minimum(t, S - 1)
+    lo = np.maximum(0, t - int(window) + 1)
+    pairs = int(np.maximum(0, hi - lo + 1).sum())
+    return 4.0 * B * Hq * pairs * d_h
+
+
 def decode_kv_bytes(seq_lens, Hkv, d_h, elem_bytes=2):
     """KV bytes a decode step must read: sum_b L_b * Hkv * d_h * 2 (K and V) * elem_bytes."""
     return int(sum(int(L) for L in seq_lens)) * Hkv * d_h * 2 * elem_bytes
@@ -125,5 +137,5 @@ def scaled(cfg, **overrides):
     return c
 
 
-__all__ = ["CONFIGS", "make_fwd_inputs", "make_decode_inputs", "fwd_flops", "decode_kv_bytes",
+__all__ = ["CONFIGS", "make_fwd_inputs", "make_decode_inputs", "fwd_flops", "window_flops", "decode_kv_bytes",
            "fwd_io_bytes", "scaled", "torch_dtype"]
