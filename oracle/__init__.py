@@ -5,7 +5,9 @@ benchmark's CPU-baseline leg, never by the product library or its binding.
 """
 
 from .attention import (apply_rope, attention, attention_rows, causal_mask, decode_paged,
-                        gather_paged, kv_head_of, max_abs, rel_rms, rope_inv_freq, sdpa)
+                        gather_paged, kv_head_of, max_abs, prefill_paged, rel_rms, rope_inv_freq, sdpa,
+                        window_mask)
 
 __all__ = ["apply_rope", "attention", "attention_rows", "causal_mask", "decode_paged",
-           "gather_paged", "kv_head_of", "max_abs", "rel_rms", "rope_inv_freq", "sdpa"]
+           "gather_paged", "kv_head_of", "max_abs", "prefill_paged", "rel_rms", "rope_inv_freq", "sdpa",
+           "window_mask"]

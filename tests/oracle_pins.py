@@ -457,6 +457,59 @@ def check_decode_equals_last_causal_row(orc):
         assert np.allclose(ld[0], l[0, :, L - 1], atol=1e-13), L
 
 
+def check_prefill_paged_equals_contiguous(orc):
+    """Prefill through block tables (K stored already rotated) equals causal prefill with RoPE
+    on contiguous K at the same positions; one new token equals the decode step; and two
+    sequences whose tables share the prefix blocks give the same result as with private
+    copies of those blocks."""
+    rng = _rng(17)
+    Hq, Hkv, d, bs, base = 4, 2, 8, 16, 10000.0
+    for (L, T) in ((40, 9), (33, 33), (70, 1), (16, 5)):
+        q = rng.standard_normal((1, Hq, T, d))
+        k = rng.standard_normal((1, Hkv, L, d))
+        v = rng.standard_normal((1, Hkv, L, d))
+        o, l = orc.attention(q, k, v, causal=True, rope_base=base, pos=L - T)
+        k_rot = orc.apply_rope(k[0], np.arange(L), base)
+        kpool, table = _scatter_paged(k_rot, bs, 3, np.random.default_rng(L + T))
+        vpool, _ = _scatter_paged(v[0], bs, 3, np.random.default_rng(L + T))
+        op, lp = orc.prefill_paged(q, kpool, vpool, table[None], np.array([L]), bs, rope_base=base)
+        assert np.allclose(op, o, atol=1e-12) and np.allclose(lp, l, atol=1e-12), (L, T)
+        if T == 1:
+            od, ld = orc.decode_paged(q[:, :, 0], kpool, vpool, table[None], np.array([L]), bs, rope_base=base)
+            assert np.allclose(od, op[:, :, 0], atol=1e-13) and np.allclose(ld, lp[:, :, 0], atol=1e-13)
+    # shared prefix: sequences 0 and 1 share their first 3 blocks
+    P, T = 48, 7
+    L0, L1 = P + 10, P + 20
+    pre_k, pre_v = rng.standard_normal((2, Hkv, P, d))
+    own_k = [rng.standard_normal((Hkv, L - P, d)) for L in (L0, L1)]
+    own_v = [rng.standard_normal((Hkv, L - P, d)) for L in (L0, L1)]
+    nb0, nb1 = -(-L0 // bs), -(-L1 // bs)
+    pool_k = np.zeros((3 + (nb0 - 3) + (nb1 - 3) + 3, Hkv, bs, d))
+    pool_v = np.zeros_like(pool_k)
+    shared = [0, 1, 2]
+    t0 = shared + [3 + i for i in range(nb0 - 3)]
+    t1 = shared + [3 + (nb0 - 3) + i for i in range(nb1 - 3)]
+    for (tab, L, ok, ov) in ((t0, L0, own_k[0], own_v[0]), (t1, L1, own_k[1], own_v[1])):
+        kk = np.concatenate([pre_k, ok], axis=1)
+        vv = np.concatenate([pre_v, ov], axis=1)
+        for j in range(L):
+            pool_k[tab[j // bs], :, j % bs] = kk[:, j]
+            pool_v[tab[j // bs], :, j % bs] = vv[:, j]
+    table = np.full((2, max(nb0, nb1)), -1, dtype=np.int32)
+    table[0, :nb0], table[1, :nb1] = t0, t1
+    q = rng.standard_normal((2, Hq, T, d))
+    lens = np.array([L0, L1])
+    os_, ls_ = orc.prefill_paged(q, pool_k, pool_v, table, lens, bs, rope_base=base)
+    for b, (tab, L) in enumerate(((t0, L0), (t1, L1))):
+        kk = orc.gather_paged(pool_k, tab, L, bs)
+        vv = orc.gather_paged(pool_v, tab, L, bs)
+        assert np.array_equal(kk[:, :P], pre_k) and np.array_equal(vv[:, :P], pre_v)
+        priv_k, priv_t = _scatter_paged(kk, bs, 1, np.random.default_rng(b))
+        priv_v, _ = _scatter_paged(vv, bs, 1, np.random.default_rng(b))
+        ob, lb = orc.prefill_paged(q[b:b + 1], priv_k, priv_v, priv_t[None], np.array([L]), bs, rope_base=base)
+        assert np.allclose(ob[0], os_[b], atol=1e-13) and np.allclose(lb[0], ls_[b], atol=1e-13)
+
+
 def check_torch_sdpa_core(orc):
     """Library cross-check of scale, mask and GQA map: torch's fp64 CPU SDPA on the
     oracle's rotated q and k must agree."""
@@ -493,6 +546,7 @@ def check_cross_attention_shapes(orc):
 
 
 ALL_CHECKS = [
+    check_prefill_paged_equals_contiguous,
     check_bruteforce_window,
     check_window_special_cases,
     check_bruteforce_tiny, check_q_zero_gives_mean, check_single_key, check_causal_first_row,
