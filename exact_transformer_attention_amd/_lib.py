@@ -15,8 +15,8 @@ LIB_PATH = os.path.join(PKG, "libattn.so")
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
 ATTN_F32, ATTN_BF16 = 0, 1
 
-EXPORTED = ("attn_fwd", "attn_fwd_window", "attn_decode_paged", "attn_decode_workspace_bytes",
-            "attn_paged_gather", "attn_status_str")
+EXPORTED = ("attn_fwd", "attn_fwd_window", "attn_prefill_paged", "attn_decode_paged",
+            "attn_decode_workspace_bytes", "attn_paged_gather", "attn_status_str")
 
 
 def _load():
@@ -29,6 +29,9 @@ def _load():
     lib.attn_fwd.restype = i32
     lib.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, f32, i64, i32, vp]
     lib.attn_fwd_window.restype = i32
+    lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp,
+                                       i32, vp]
+    lib.attn_prefill_paged.restype = i32
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp,
                                       vp, sz, i32, vp]
     lib.attn_decode_paged.restype = i32
@@ -121,6 +124,32 @@ def attn_fwd_window(q, k, v, window, rope_base=0.0, pos=0, out=None, lse=None, w
     st = LIB.attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, T, S, d,
                              int(window), float(rope_base), int(pos), _dtype_code(q), _stream(stream))
     _check(st, "attn_fwd_window")
+    return out, lse
+
+
+def attn_prefill_paged(q, k_cache, v_cache, block_table, seq_lens, block_size=16, rope_base=0.0, out=None,
+                       lse=None, want_lse=True, stream=None):
+    """Prefill of the last T tokens of each sequence over a paged cache.  q [N,Hq,T,d_h];
+    caches [num_blocks,Hkv,block_size,d_h]; block_table [N,max_blocks] int32; seq_lens [N]
+    int32 (all device tensors).  Returns (out [N,Hq,T,d_h], lse [N,Hq,T])."""
+    import torch
+    _require(q.dim() == 4, "q must be [N, Hq, T, d_h]")
+    N, Hq, T, d = q.shape
+    num_blocks, Hkv = k_cache.shape[0], k_cache.shape[1]
+    _require(k_cache.shape == v_cache.shape and k_cache.shape[2] == block_size and k_cache.shape[3] == d,
+             "cache shape mismatch")
+    _require(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables must be int32")
+    _require(block_table.dim() == 2 and block_table.shape[0] == N and seq_lens.shape == (N,), "table shape")
+    for t in (q, k_cache, v_cache, block_table, seq_lens):
+        _require(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((N, Hq, T), dtype=torch.float32, device=q.device)
+    st = LIB.attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                block_size, N, Hq, Hkv, d, T, block_table.shape[1], num_blocks, float(rope_base),
+                                _ptr(out), _ptr(lse), _dtype_code(q), _stream(stream))
+    _check(st, "attn_prefill_paged")
     return out, lse
 
 

@@ -95,6 +95,46 @@ attn_status_t attn_fwd_window(const void* q, const void* k, const void* v, void*
   return fwd_impl(q, k, v, out, lse, B, Hq, Hkv, T, S, d_h, 1, window, rope_base, pos, dtype, stream);
 }
 
+attn_status_t attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                                 int num_seqs, int Hq, int Hkv, int d_h, int T, int max_blocks_per_seq,
+                                 int num_blocks, float rope_base, void* out, float* lse, attn_dtype_t dtype,
+                                 void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return ATTN_ERR_INVALID_ARG;
+  if (num_seqs < 1 || Hq < 1 || Hkv < 1 || d_h < 1 || T < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      block_size < 1)
+    return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (bad_base(rope_base)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16 || d_h != 128 || block_size != attn::kPageBlock ||
+      max_blocks_per_seq > attn::kMaxPagedBlocks)
+    return ATTN_ERR_UNSUPPORTED;
+
+  attn::FwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.out = out;
+  p.lse = lse;
+  p.B = num_seqs;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.T = T;
+  p.S = max_blocks_per_seq * block_size;
+  p.causal = 1;
+  p.paged = 1;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.use_rope = rope_base > 0.f;
+  fill_rope(p.rope_c, d_h, p.use_rope ? rope_base : 1.f);
+  hipError_t e = attn::launch_fwd_bf16(p, d_h, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_h, int max_blocks_per_seq,
                                    int block_size) {
   if (num_seqs < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d_h < 1 || max_blocks_per_seq < 1 ||

@@ -224,6 +224,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   // Direct loads of the block at physical index phys (KV head kvh) into stage st: load r
   // covers token rows 4r .. 4r+3.
   auto issue = [&](int phys, int kvh, int st) {
+    phys = min(max(phys, 0), p.num_blocks - 1);  // a bad table entry never leaves the pool
     const size_t sl = slice_offset(phys, Hkv, kvh, kDecD);
     char* kdst = ring + st * kStageBytes;
     char* vdst = kdst + kStageBytes / 2;

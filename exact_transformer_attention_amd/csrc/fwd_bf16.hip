@@ -100,13 +100,18 @@ __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(
 
 }  // namespace
 
-template <int D, int HP, bool ROPE>
+// PAGED: K and V come from a block-tabled cache ([blocks, Hkv, 16, D], as the decode
+// kernels read it), sequence b holding seq_lens[b] tokens whose last T are the queries;
+// cached K is already rotated, so only Q is rotated (at its positions).
+template <int D, int HP, bool ROPE, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kNW / 4, kNW / 4)))
 void fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<D>;
+  constexpr bool ROTK = ROPE && !PAGED;  // rotate K at load
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][kBN * C::KSTR];   // rotated K, padded rows
   __shared__ __attribute__((aligned(16))) u32x4 Vs[2][kBN * C::CPR];     // V, swizzled 16-byte chunks
   __shared__ __attribute__((aligned(16))) u32x4 Kraw[2][kBN * C::CPR];   // K as loaded
+  __shared__ int32_t tbl[PAGED ? kMaxPagedBlocks : 1];                     // block table row
 
   const int tid = threadIdx.x;
   const int wid = tid / kWave;
@@ -132,13 +137,21 @@ void fwd_bf16_kernel(FwdParams p) {
   const int b = grp / hpg;
   const int hq = (grp % hpg) * HP + wid / (kNW / HP);
   const int kvh = ((grp % hpg) * HP) / (p.Hq / p.Hkv);
-  const int T = p.T, S = p.S;
+  const int T = p.T;
+  int S = p.S;
+  int64_t pos = p.pos;
+  if constexpr (PAGED) {  // this sequence's keys; its queries are its last T tokens
+    S = min(p.seq_lens[b], p.max_blocks_per_seq * kPageBlock);
+    pos = (int64_t)S - T;
+    const int nblk = (S + kPageBlock - 1) / kPageBlock;
+    for (int i = tid; i < nblk; i += kThreads) tbl[i] = p.block_table[(size_t)b * p.max_blocks_per_seq + i];
+    __syncthreads();
+  }
   const int wrow0 = qb * RH + (wid % (kNW / HP)) * kQW;  // first query row of this wave
-  const int64_t pos = p.pos;
 
   const __bf16* qg = (const __bf16*)p.q + ((size_t)b * p.Hq + hq) * (size_t)T * D;
-  const __bf16* kg = (const __bf16*)p.k + ((size_t)b * p.Hkv + kvh) * (size_t)S * D;
-  const __bf16* vg = (const __bf16*)p.v + ((size_t)b * p.Hkv + kvh) * (size_t)S * D;
+  const __bf16* kg = (const __bf16*)p.k + (PAGED ? 0 : ((size_t)b * p.Hkv + kvh) * (size_t)S * D);
+  const __bf16* vg = (const __bf16*)p.v + (PAGED ? 0 : ((size_t)b * p.Hkv + kvh) * (size_t)S * D);
 
   // ---- keys visible to this wave / to the workgroup.
   int nk_wave = S, nk_wg = S;
@@ -199,7 +212,7 @@ void fwd_bf16_kernel(FwdParams p) {
   // tile*64 + row0, plus the per-row and per-block steps.
   float ac[4], as[4], rc[4], rs[4], tc[4], ts[4];
   double cturn[4];
-  if constexpr (ROPE) {
+  if constexpr (ROTK) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       cturn[e] = p.rope_c[slot * 4 + e];
@@ -222,13 +235,36 @@ void fwd_bf16_kernel(FwdParams p) {
   auto block_rsrc = [&](const __bf16* base, int k0) {
     return make_rsrc(base + (size_t)k0 * D, (uint32_t)(S - k0) * D * 2);
   };
+  // Paged: the cache element offset of key row `key` (clamped to a stored row: rows past
+  // S are never visible), through the block table row held in LDS.
+  auto paged_row = [&](int key) -> size_t {
+    key = min(key, S - 1);
+    const int phys = min(max(tbl[key / kPageBlock], 0), p.num_blocks - 1);  // never outside the pool
+    return (((size_t)phys * p.Hkv + kvh) * kPageBlock + key % kPageBlock) * (size_t)D;
+  };
   auto load_k = [&](int tile) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int j = 0; j < C::NCH; ++j)
+        load_lds16(kg + paged_row(tile * kBN + row0 + j * C::RSTEP) + slot * 8,
+                   &Kraw[tile & 1][(wid * C::NCH + j) * kWave]);
+      return;
+    }
     const i32x4 rs = block_rsrc(kg, tile * kBN);
 #pragma unroll
     for (int j = 0; j < C::NCH; ++j)
       buffer_load_lds16(rs, koff[j], &Kraw[tile & 1][(wid * C::NCH + j) * kWave]);
   };
   auto load_v = [&](int tile) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int j = 0; j < C::NCH; ++j) {
+        const int r = row0 + j * C::RSTEP;
+        load_lds16(vg + paged_row(tile * kBN + r) + (slot ^ vswz<D>(r)) * 8,
+                   &Vs[tile & 1][(wid * C::NCH + j) * kWave]);
+      }
+      return;
+    }
     const i32x4 rs = block_rsrc(vg, tile * kBN);
 #pragma unroll
     for (int j = 0; j < C::NCH; ++j)
@@ -238,7 +274,7 @@ void fwd_bf16_kernel(FwdParams p) {
   // waited for the loads of that block.
   auto rotate_k = [&](int tile, auto kbc) {
     constexpr int kb = decltype(kbc)::value;  // == tile & 1
-    if constexpr (ROPE) {
+    if constexpr (ROTK) {
       float c[4], s[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -269,7 +305,7 @@ void fwd_bf16_kernel(FwdParams p) {
   // Exact angles of this thread's first key of block `tile` (every kResync blocks; the
   // angle addition in rotate_k advances them in between).
   auto resync = [&](int tile, bool force = false) {
-    if constexpr (ROPE) {
+    if constexpr (ROTK) {
       if (force || tile % kResync == 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -349,7 +385,7 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int j = 0; j < C::NCH; ++j) raw[j] = Kraw[kn][(wid * C::NCH + j) * kWave + lane];
     float c[4], sn[4];
-    if constexpr (ROPE) {
+    if constexpr (ROTK) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         c[e] = ac[e];
@@ -375,7 +411,7 @@ void fwd_bf16_kernel(FwdParams p) {
           s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][mb], qop[nb][ks], s[mb][nb], 0, 0, 0);
       // rotation unit ks: pair slot e of chunk j
       const int j = ks / 4, e = ks % 4;
-      if constexpr (ROPE) {
+      if constexpr (ROTK) {
         const float x0 = bf16_lo(raw[j][e]), x1 = bf16_hi(raw[j][e]);
         out[j][e] = pack_bf16(x0 * c[e] - x1 * sn[e], x0 * sn[e] + x1 * c[e]);
         if (j + 1 < C::NCH) cmul(c[e], sn[e], rc[e], rs[e]);
@@ -569,7 +605,7 @@ void fwd_bf16_kernel(FwdParams p) {
 }
 
 namespace {
-template <int D, int HP, bool ROPE>
+template <int D, int HP, bool ROPE, bool PAGED>
 hipError_t launch_one(FwdParams q, hipStream_t stream) {
   constexpr int RH = kNW * kQW / HP;
   q.n_qblocks = (q.T + RH - 1) / RH;
@@ -577,13 +613,17 @@ hipError_t launch_one(FwdParams q, hipStream_t stream) {
   q.xcd_remap = (q.n_groups % 8) == 0;
   const long long grid = (long long)q.n_qblocks * q.n_groups;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, HP, ROPE>), dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, HP, ROPE, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 
 template <int D, int HP>
 hipError_t launch_r(const FwdParams& p, hipStream_t stream) {
-  return p.use_rope ? launch_one<D, HP, true>(p, stream) : launch_one<D, HP, false>(p, stream);
+  if constexpr (D == 128) {
+    if (p.paged)
+      return p.use_rope ? launch_one<D, HP, true, true>(p, stream) : launch_one<D, HP, false, true>(p, stream);
+  }
+  return p.use_rope ? launch_one<D, HP, true, false>(p, stream) : launch_one<D, HP, false, false>(p, stream);
 }
 
 template <int D>

@@ -5,7 +5,9 @@
 
 namespace attn {
 
-constexpr int kMaxHalfDim = 64;  // d_h <= 128
+constexpr int kMaxHalfDim = 64;        // d_h <= 128
+constexpr int kPageBlock = 16;         // tokens per cache block (paged prefill)
+constexpr int kMaxPagedBlocks = 4096;  // block-table entries a paged prefill holds on chip
 
 struct FwdParams {
   const void* q;
@@ -17,6 +19,12 @@ struct FwdParams {
   int causal;
   int use_rope;
   int64_t window;  // > 0: causal sliding window, key s visible iff pos + t - window < s <= pos + t
+  // paged prefill (k, v are block-tabled caches [blocks, Hkv, 16, d_h]; S and pos per sequence)
+  int paged;
+  const int32_t* block_table;  // [B, max_blocks_per_seq]
+  const int32_t* seq_lens;     // [B] cached tokens, the last T of them being the queries
+  int max_blocks_per_seq;
+  int num_blocks;
   int n_qblocks;  // query blocks per (batch, head group)
   int n_groups;   // batch * head groups
   int xcd_remap;  // 1 if n_groups is a multiple of 8 (see work mapping in the kernel)

@@ -104,7 +104,8 @@ ATTN_API attn_status_t attn_fwd_window(const void* q, const void* k, const void*
  *                entries past the sequence are ignored
  *   seq_lens     [num_seqs] int32: cached tokens per sequence (current one included);
  *                device contract: 1 <= seq_lens[b] <= max_blocks_per_seq * block_size and
- *                every used table entry in [0, num_blocks) (not checked on the device)
+ *                every used table entry in [0, num_blocks) (entries outside are clamped into
+ *                the pool: no fault, but that sequence's result is undefined)
  *   out          [num_seqs, Hq, d_h] dtype `dtype`;  lse [num_seqs, Hq] fp32 or NULL
  *   workspace    device scratch of at least attn_decode_workspace_bytes(...) bytes for
  *                the partial results; caller-owned, contents need no clearing; two calls
@@ -123,6 +124,35 @@ ATTN_API attn_status_t attn_decode_paged(const void* q, const void* k_cache, con
                                 int max_blocks_per_seq, int num_blocks, float rope_base,
                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
                                 attn_dtype_t dtype, void* stream);
+
+/*
+ * attn_prefill_paged -- prefill (or chunked prefill) of T new query tokens per sequence
+ * whose keys and values, including any shared prefix, sit in a block-tabled cache
+ * ("Self-Attention Complexity, FlashAttention, PagedAttention, and RoPE in Code", Part 3:
+ * fixed-size blocks, per-sequence block tables, and blocks shared between sequences that
+ * have a common prefix).  Several block tables may name the same physical blocks; the
+ * kernel only reads the cache.
+ *
+ *   q            [num_seqs, Hq, T, d_h]: the last T tokens of each sequence; query row t of
+ *                sequence b sits at position seq_lens[b] - T + t and is rotated there when
+ *                rope_base > 0
+ *   k_cache, v_cache, block_table, seq_lens, block_size, max_blocks_per_seq, num_blocks
+ *                as for attn_decode_paged (cached K already rotated; seq_lens[b] counts the
+ *                new tokens, whose K and V the caller has written into the cache)
+ *   out          [num_seqs, Hq, T, d_h] bf16;  lse [num_seqs, Hq, T] fp32 or NULL
+ * Key s is visible to query row t iff s <= seq_lens[b] - T + t (causal over the whole
+ * sequence).  Device contract: T <= seq_lens[b] <= max_blocks_per_seq * block_size (rows
+ * whose position is negative get output 0 and lse -inf); table entries outside
+ * [0, num_blocks) are clamped into the pool (no fault; such a sequence's result is
+ * undefined).
+ * Supported: bf16, d_h == 128, block_size == 16, max_blocks_per_seq <= 4096, Hq % Hkv == 0.
+ */
+ATTN_API attn_status_t attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          int block_size, int num_seqs, int Hq, int Hkv, int d_h,
+                                          int T, int max_blocks_per_seq, int num_blocks,
+                                          float rope_base, void* out, float* lse, attn_dtype_t dtype,
+                                          void* stream);
 
 /* Bytes of workspace attn_decode_paged needs for these sizes (0 on invalid sizes). */
 ATTN_API size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_h,

@@ -214,32 +214,34 @@ def attention_rows(q, k, v, rows, causal=False, rope_base=0.0, pos=0, window=0):
 
 # ------------------------------------------------------------- decode ----
 
-def prefill_paged(q, k_cache, v_cache, block_table, seq_lens, block_size, rope_base=0.0):
+def prefill_paged(q, k_cache, v_cache, block_table, seq_lens, block_size, rope_base=0.0, heads=None):
     """Prefill of the last T tokens of each sequence against its block-tabled cache
     ("Self-Attention Complexity, FlashAttention, PagedAttention, and RoPE in Code", Part 3).
 
     q [N, Hq, T, d_h]; caches [num_blocks, Hkv, block_size, d_h]; block_table [N, max_blocks];
     seq_lens [N] (tokens per sequence, the new ones included).  Query row t of sequence b sits
     at position L_b - T + t and is rotated there; cached K is used as stored (already rotated);
-    key s is visible iff s <= L_b - T + t.  Returns (out [N, Hq, T, d_h], lse [N, Hq, T]).
+    key s is visible iff s <= L_b - T + t.  Returns (out [N, Hq, T, d_h], lse [N, Hq, T]);
+    with heads given, only those query heads, in that order (for sampling large cases).
     """
     q = np.asarray(q, dtype=F64)
     N, Hq, T, d_h = q.shape
     Hkv = k_cache.shape[1]
-    out = np.zeros((N, Hq, T, v_cache.shape[3]), dtype=F64)
-    lse = np.zeros((N, Hq, T), dtype=F64)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    out = np.zeros((N, len(heads), T, v_cache.shape[3]), dtype=F64)
+    lse = np.zeros((N, len(heads), T), dtype=F64)
     for b in range(N):
         L = int(seq_lens[b])
         kb = gather_paged(k_cache, block_table[b], L, block_size).astype(F64)   # [Hkv, L, d]
         vb = gather_paged(v_cache, block_table[b], L, block_size).astype(F64)
         qpos = (L - T) + np.arange(T, dtype=np.int64)
         mask = causal_mask(qpos, np.arange(L, dtype=np.int64))
-        for h in range(Hq):
+        for i, h in enumerate(heads):
             g = kv_head_of(h, Hq, Hkv)
             qr = apply_rope(q[b, h], qpos, rope_base)
             o, l, _ = sdpa(qr, kb[g], vb[g], mask)
-            out[b, h] = o
-            lse[b, h] = l
+            out[b, i] = o
+            lse[b, i] = l
     return out, lse
 
 

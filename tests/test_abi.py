@@ -24,8 +24,8 @@ def lib():
 
 def test_header_declares_entry_points():
     names = header_functions()
-    assert names == sorted(["attn_fwd", "attn_fwd_window", "attn_decode_paged", "attn_decode_workspace_bytes",
-                            "attn_paged_gather", "attn_status_str"])
+    assert names == sorted(["attn_fwd", "attn_fwd_window", "attn_prefill_paged", "attn_decode_paged",
+                            "attn_decode_workspace_bytes", "attn_paged_gather", "attn_status_str"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -103,6 +103,24 @@ def dec(lib, **kw):
 ])
 def test_decode_validation(lib, kw, status):
     assert dec(lib, **kw) == status
+
+
+def prefill_paged(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, bs=16, N=4, Hq=32, Hkv=8, d=128, T=64, mbps=10, nb=40,
+             base=10000.0, out=FAKE, lse=None, dtype=1)
+    a.update(kw)
+    return lib.attn_prefill_paged(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["bs"], a["N"], a["Hq"], a["Hkv"],
+                                  a["d"], a["T"], a["mbps"], a["nb"], a["base"], a["out"], a["lse"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(kc=None), 1), (dict(bt=None), 1), (dict(sl=None), 1), (dict(out=None), 1),
+    (dict(N=0), 1), (dict(T=0), 1), (dict(Hq=30), 1), (dict(mbps=0), 1), (dict(nb=0), 1), (dict(base=-1.0), 1),
+    (dict(dtype=4), 1),
+    (dict(dtype=0), 2), (dict(d=64), 2), (dict(bs=32), 2), (dict(mbps=4097), 2),
+])
+def test_prefill_paged_validation(lib, kw, status):
+    assert prefill_paged(lib, **kw) == status
 
 
 def test_workspace_bytes(lib):

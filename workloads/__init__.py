@@ -31,6 +31,10 @@ import torch
 
 # name -> parameters.  "seed" is fixed per workload.
 CONFIGS = {
+    # prefill of 1024 new tokens per sequence over a paged cache whose first 6144 tokens are
+    # one shared prefix (chunked prefill with a prefix cache)
+    "prefix8": dict(num_seqs=8, Hq=32, Hkv=8, d_h=128, T=1024, prefix_len=6144, extra_lens=[0] * 8,
+                    rope_base=10000.0, sigma=1.0, seed=6),
     "small_f32": dict(kind="fwd", dtype="f32", B=1, Hq=1, Hkv=1, T=128, S=128, d_h=64,
                       causal=False, rope_base=0.0, pos=0, sigma=1.0, seed=1),
     "mha2k": dict(kind="fwd", dtype="bf16", B=4, Hq=32, Hkv=32, T=2048, S=2048, d_h=128,
@@ -103,6 +107,63 @@ def make_decode_inputs(num_seqs, Hq, Hkv, d_h, block_size=16, len_lo=512, len_hi
                 num_blocks=num_blocks, max_blocks_per_seq=block_table.shape[1])
 
 
+def make_prefill_paged_inputs(num_seqs, Hq, Hkv, d_h, T, prefix_len, extra_lens, block_size=16, dtype="bf16",
+                              sigma=1.0, seed=0, shared=True, device=None, **_):
+    """Paged caches for a prefill of the last T tokens of each sequence, the sequences
+    starting with a common prefix of prefix_len tokens.
+
+    Sequence b holds prefix_len + extra_lens[b] + T tokens.  With shared=True the
+    prefix_len // block_size full prefix blocks are one set of physical blocks named by
+    every table; the rest of the prefix (a partial block) is copied into each sequence's
+    own first block.  With shared=False every sequence has private copies of the same
+    values.  Draw order (generator seeded with seed, on `device` if given): prefix K and V
+    [Hkv, prefix_len, d_h], then per sequence its own K and V [Hkv, extra + T, d_h], then
+    q [num_seqs, Hq, T, d_h], all N(0, sigma^2) rounded to dtype; then the pool
+    permutation from a host generator seeded with seed + 1.
+    """
+    td = _TORCH_DTYPE[dtype]
+    dev = device if device is not None else "cpu"
+    g = torch.Generator(dev).manual_seed(int(seed))
+    bs = block_size
+    lens = [prefix_len + int(e) + T for e in extra_lens]
+
+    def draw(shape):
+        return (torch.randn(shape, generator=g, dtype=torch.float32, device=dev) * sigma).to(td)
+
+    pk, pv = draw((Hkv, prefix_len, d_h)), draw((Hkv, prefix_len, d_h))
+    own = [(draw((Hkv, L - prefix_len, d_h)), draw((Hkv, L - prefix_len, d_h))) for L in lens]
+    q = draw((num_seqs, Hq, T, d_h))
+
+    nshared = prefix_len // bs if shared else 0
+    nblk = [(L + bs - 1) // bs for L in lens]
+    num_blocks = nshared + sum(n - nshared for n in nblk)
+    perm = torch.randperm(num_blocks, generator=torch.Generator("cpu").manual_seed(int(seed) + 1))
+    table = torch.full((num_seqs, max(nblk)), -1, dtype=torch.int32)
+    off = nshared
+    for b in range(num_seqs):
+        table[b, :nshared] = perm[:nshared].to(torch.int32)
+        n = nblk[b] - nshared
+        table[b, nshared:nblk[b]] = perm[off:off + n].to(torch.int32)
+        off += n
+    k_cache = torch.zeros((num_blocks, Hkv, bs, d_h), dtype=td, device=dev)
+    v_cache = torch.zeros_like(k_cache)
+    tab = table.to(dev).long()
+    for b in range(num_seqs):
+        kk, vv = torch.cat([pk, own[b][0]], dim=1), torch.cat([pv, own[b][1]], dim=1)
+        j = torch.arange(nshared * bs if b > 0 else 0, lens[b], device=dev)
+        phys = tab[b][j // bs]
+        k_cache[phys, :, j % bs] = kk[:, j].transpose(0, 1)
+        v_cache[phys, :, j % bs] = vv[:, j].transpose(0, 1)
+    return dict(q=q, k_cache=k_cache, v_cache=v_cache, block_table=table,
+                seq_lens=torch.tensor(lens, dtype=torch.int32), block_size=bs, num_blocks=num_blocks, T=T)
+
+
+def prefill_paged_flops(seq_lens, Hq, T, d_h):
+    """4*d_h per visible (query, key) pair: query t of sequence b sees L_b - T + t + 1 keys."""
+    pairs = sum(T * (int(L) - T) + T * (T + 1) // 2 for L in seq_lens)
+    return 4.0 * Hq * pairs * d_h
+
+
 def fwd_flops(B, Hq, T, S, d_h, causal, **_):
     """Algorithmic FLOPs of one forward: 4*B*Hq*T*S*d_h, halved when causal."""
     f = 4.0 * B * Hq * T * S * d_h
@@ -137,5 +198,6 @@ def scaled(cfg, **overrides):
     return c
 
 
-__all__ = ["CONFIGS", "make_fwd_inputs", "make_decode_inputs", "fwd_flops", "window_flops", "decode_kv_bytes",
+__all__ = ["CONFIGS", "make_fwd_inputs", "make_decode_inputs", "make_prefill_paged_inputs", "fwd_flops",
+           "window_flops", "prefill_paged_flops", "decode_kv_bytes",
            "fwd_io_bytes", "scaled", "torch_dtype"]
