@@ -55,7 +55,7 @@ def measured_traffic(kind, digest):
     return t.get("hbm_bytes_per_launch")
 
 
-def summarize_pmc(fetch_csv, write_csv, out_dir, window_run=False):
+def summarize_pmc(fetch_csv, write_csv, out_dir, extra_kind=None):
     """Per-launch HBM traffic of the timed kernels from two rocprofv3 --pmc runs (FETCH_SIZE,
     then WRITE_SIZE; kilobytes per dispatch), scaled by the factor the same counters read
     for a plain 1 GiB device copy (run with --copy-calibration).  Writes
@@ -97,14 +97,14 @@ def summarize_pmc(fetch_csv, write_csv, out_dir, window_run=False):
     w_scale = copy_bytes / w_copy if w_copy else 1.0
     res = {"calibration": {"kernel": "1 GiB device copy", "fetch_raw_bytes": f_copy, "write_raw_bytes": w_copy,
                            "fetch_scale": f_scale, "write_scale": w_scale}}
-    kinds = ((("window", ["fwd_bf16_kernel"], PREFILL_SOURCES),) if window_run else
+    kinds = (((extra_kind, ["fwd_bf16_kernel"], PREFILL_SOURCES),) if extra_kind else
              (("prefill", ["fwd_bf16_kernel"], PREFILL_SOURCES),
               ("decode", ["decode_partial_kernel", "decode_merge_kernel"], DECODE_SOURCES)))
     path = os.path.join(out_dir, "traffic.json")
-    if window_run and os.path.exists(path):  # a window run adds its entry to the main one
+    if extra_kind and os.path.exists(path):  # a window or prefix run adds its entry to the main one
         with open(path) as f:
             old = json.load(f)
-        old["window_calibration"] = res["calibration"]
+        old[extra_kind + "_calibration"] = res["calibration"]
         res = old
     for kind, keys, srcs in kinds:
         fb = [pick(fetch, k) for k in keys]
@@ -239,6 +239,76 @@ def window_bench(a):
     print(json.dumps(res), flush=True)
 
 
+def prefix_bench(a):
+    """Paged prefill of 1024 new tokens per sequence, 8 sequences over one shared 6144-token
+    prefix (one JSON line)."""
+    import torch
+    import workloads
+    from exact_transformer_attention_amd import attn_prefill_paged
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS["prefix8"]
+    d = workloads.make_prefill_paged_inputs(**cfg)
+    q, kc, vc = d["q"].to(dev), d["k_cache"].to(dev), d["v_cache"].to(dev)
+    bt, sl = d["block_table"].to(dev), d["seq_lens"].to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def run():
+        attn_prefill_paged(q, kc, vc, bt, sl, block_size=16, rope_base=cfg["rope_base"], out=out, lse=lse)
+
+    for _ in range(a.warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    avg = sum(ms) / len(ms)
+    assert bool(torch.isfinite(out).all())
+    if a.copy_calibration:
+        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+    lens = d["seq_lens"].tolist()
+    flops = workloads.prefill_paged_flops(lens, cfg["Hq"], cfg["T"], cfg["d_h"])
+    tf = flops / (avg * 1e-3) / 1e12
+    res = {
+        "metric": "paged prefill (shared prefix) TFLOP/s + % bf16 MFMA peak",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(avg, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded iid normal, bf16-rounded)",
+        "config": {"workload": "paged prefill: 8 sequences x 1024 new tokens over one shared 6144-token prefix, "
+                               "Hq=32 Hkv=8 d_h=128 block 16, RoPE 1e4 on q", "cache_blocks": d["num_blocks"]},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("prefix", kernel_sources_digest(PREFILL_SOURCES)),
+                     "kernel": "fwd_bf16_kernel<128,4,paged>", "flop_per_launch": flops,
+                     "avg_launch_ms": round(avg, 4)},
+    }
+    if not a.no_cpu_baseline:
+        import oracle
+        print("[bench] timing the oracle on the host (prefix sample)", file=sys.stderr, flush=True)
+        heads = list(range(8))
+        qs = d["q"][:1].double().numpy()
+        t0 = time.perf_counter()
+        oracle.prefill_paged(qs, d["k_cache"].double().numpy(), d["v_cache"].double().numpy(),
+                             d["block_table"][:1].numpy(), d["seq_lens"][:1].numpy(), 16, rope_base=cfg["rope_base"],
+                             heads=heads)
+        dt = time.perf_counter() - t0
+        sf = workloads.prefill_paged_flops(lens[:1], len(heads), cfg["T"], cfg["d_h"])
+        res["cpu_baseline"] = dict(value=sf / dt / 1e12, unit="TFLOP/s", cores=cpu_threads(), kind="oracle",
+                                   seconds=round(dt, 3),
+                                   sample=f"sequence 0, query heads 0-7, all {cfg['T']} new rows, fp64 numpy; "
+                                          f"{sf:.3e} algorithmic FLOP")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,17 +317,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "decode", "window"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "window", "prefix"], default=None,
                     help="time only one part (profiling runs); 'window' times the causal sliding-window "
-                         "prefill (attn_fwd_window) on the same 8192-token GQA workload instead")
+                         "prefill (attn_fwd_window) on the same 8192-token GQA workload instead; 'prefix' "
+                         "the paged prefill (attn_prefill_paged) of 8 sequences over a shared 6144-token prefix")
     ap.add_argument("--window", type=int, default=4096, help="window of --only window (keys)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/traffic.json "
-                         "(with --only window: CSVs of a window run, added as the 'window' entry)")
+                         "(with --only window or prefix: CSVs of that run, added as its own entry)")
     a = ap.parse_args()
     if a.traffic_from:
         print(json.dumps(summarize_pmc(a.traffic_from[0], a.traffic_from[1], os.path.join(ROOT, "profiles"),
-                                       window_run=a.only == "window"), indent=1))
+                                       extra_kind=a.only if a.only in ("window", "prefix") else None),
+                         indent=1))
         return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the kernels are "
@@ -266,6 +338,9 @@ def main():
 
     if a.only == "window":
         window_bench(a)
+        return
+    if a.only == "prefix":
+        prefix_bench(a)
         return
 
     import torch
