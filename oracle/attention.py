@@ -212,6 +212,73 @@ def attention_rows(q, k, v, rows, causal=False, rope_base=0.0, pos=0, window=0):
     return out, lse
 
 
+# ----------------------------------------------------------- backward ----
+
+def apply_rope_transpose(x, positions, base):
+    """The transpose (inverse) of apply_rope: rotate each pair by -phi.  The gradient with
+    respect to the unrotated vector is this map applied to the gradient with respect to the
+    rotated one (the rotation is orthogonal)."""
+    x = np.asarray(x, dtype=F64)
+    if base is None or base <= 0:
+        return x.copy()
+    d_h = x.shape[-1]
+    pos = np.asarray(positions, dtype=np.int64).astype(F64)
+    phi = pos[:, None] * rope_inv_freq(d_h, base)[None, :]
+    c, s = np.cos(phi), np.sin(phi)
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c + x1 * s
+    out[..., 1::2] = -x0 * s + x1 * c
+    return out
+
+
+def attention_backward(q, k, v, dout, causal=False, rope_base=0.0, pos=0, window=0):
+    """Gradients of sum(dout * attention(q, k, v)) with respect to q, k and v.
+
+    The forward is recomputed in full (scores, mask, softmax) from the inputs; then, with
+    S = q' k'^T / sqrt(d_h), P = softmax(S), O = P v (q', k' the rotated inputs):
+        dv  = P^T dO
+        dP  = dO v^T
+        dS  = P * (dP - rowsum(dO * O))        (the softmax Jacobian applied row by row)
+        dq' = dS k' / sqrt(d_h),   dk' = dS^T q' / sqrt(d_h)
+        dq  = R^T dq',             dk  = R^T dk'  (RoPE is a rotation: its transpose)
+    With grouped-query attention a KV head's dk and dv sum over the query heads reading it.
+    The pages state only that the backward pass recomputes the scores from the saved
+    statistics rather than storing P ("Why is attention O(n^2) ...", Deep dive:
+    FlashAttention; "Self-Attention Complexity, FlashAttention, PagedAttention, and RoPE in
+    Code", Part 2); the derivatives are the standard chain rule of the forward.
+    Returns (dq [B,Hq,T,d_h], dk [B,Hkv,S,d_h], dv [B,Hkv,S,d_h]) in float64.
+    """
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    dout = np.asarray(dout, dtype=F64)
+    B, Hq, T, d_h = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    qpos = pos + np.arange(T, dtype=np.int64)
+    kpos = np.arange(S, dtype=np.int64)
+    kr = apply_rope(k, kpos, rope_base)
+    mask = _mask(qpos, kpos, causal, window)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    scale = 1.0 / np.sqrt(F64(d_h))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            qr = apply_rope(q[b, h], qpos, rope_base)
+            o, _, p = sdpa(qr, kr[b, g], v[b, g], mask)
+            do = dout[b, h]
+            dv[b, g] += p.T @ do
+            dp = do @ v[b, g].T
+            delta = np.sum(do * o, axis=-1, keepdims=True)
+            ds = p * (dp - delta)
+            dq[b, h] = apply_rope_transpose(ds @ kr[b, g] * scale, qpos, rope_base)
+            dk[b, g] += apply_rope_transpose(ds.T @ qr * scale, kpos, rope_base)
+    return dq, dk, dv
+
+
 # ------------------------------------------------------------- decode ----
 
 def prefill_paged(q, k_cache, v_cache, block_table, seq_lens, block_size, rope_base=0.0, heads=None):

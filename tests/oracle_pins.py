@@ -545,7 +545,105 @@ def check_cross_attention_shapes(orc):
     assert np.allclose(o2[0], o[0, 1, 2], atol=1e-14) and np.allclose(o2[1], o[0, 0, 0], atol=1e-14)
 
 
+# ------------------------------------------------------------------------
+# Backward pass: gradients of sum(dO * O) with respect to q, k and v.
+# ------------------------------------------------------------------------
+
+def _bwd_case(rng, B, Hq, Hkv, T, S, d):
+    return (rng.standard_normal((B, Hq, T, d)), rng.standard_normal((B, Hkv, S, d)),
+            rng.standard_normal((B, Hkv, S, d)), rng.standard_normal((B, Hq, T, d)))
+
+
+def check_backward_finite_differences(orc):
+    """Central differences of L = sum(dO * attention(q, k, v)) through the (separately pinned)
+    forward agree with the backward's gradient, entry by entry, for causal, windowed, RoPE
+    and grouped-query cases."""
+    rng = _rng(30)
+    eps = 1e-5
+    for (Hq, Hkv, T, S, causal, base, pos, window) in ((2, 1, 5, 5, True, 10000.0, 0, 0),
+                                                        (4, 2, 4, 7, False, 100.0, 0, 0),
+                                                        (2, 2, 6, 9, True, 50.0, 3, 4)):
+        q, k, v, do = _bwd_case(rng, 1, Hq, Hkv, T, S, 8)
+        dq, dk, dv = orc.attention_backward(q, k, v, do, causal, base, pos, window)
+
+        def loss(q_, k_, v_):
+            o, _ = orc.attention(q_, k_, v_, causal=causal, rope_base=base, pos=pos, window=window)
+            return float(np.sum(do * o))
+
+        for which, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            for _ in range(6):
+                idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[which]
+                args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[which]
+                fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+                assert abs(fd - g[idx]) < 1e-7 * max(1.0, abs(fd)), (which, idx, fd, g[idx])
+
+
+def _torch_rope(x, positions, base):
+    """RoPE written with torch ops (differentiable) from the pair rotation definition."""
+    if base <= 0:
+        return x
+    d = x.shape[-1]
+    i = torch.arange(d // 2, dtype=torch.float64)
+    ang = torch.as_tensor(np.asarray(positions, dtype=np.float64))[:, None] * base ** (-2.0 * i / d)[None, :]
+    c, s = torch.cos(ang), torch.sin(ang)
+    a, b = x[..., 0::2], x[..., 1::2]
+    return torch.stack((a * c - b * s, a * s + b * c), dim=-1).flatten(-2)
+
+
+def check_backward_torch_autograd(orc):
+    """Library cross-check: torch autograd through torch's fp64 CPU SDPA, fed by a torch RoPE,
+    gives the same dq, dk and dv (grouped-query sums included)."""
+    rng = _rng(31)
+    for (Hq, Hkv, T, S, causal, base, pos) in ((4, 2, 9, 9, True, 10000.0, 0), (4, 1, 5, 12, False, 500.0, 0),
+                                               (2, 2, 6, 10, True, 10000.0, 4)):
+        q, k, v, do = _bwd_case(rng, 2, Hq, Hkv, T, S, 16)
+        dq, dk, dv = orc.attention_backward(q, k, v, do, causal, base, pos)
+        qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        qr = _torch_rope(qt, pos + np.arange(T), base)
+        kr = _torch_rope(kt, np.arange(S), base)
+        mask = None
+        if causal:
+            mask = torch.from_numpy(np.arange(S)[None, :] <= (pos + np.arange(T))[:, None])
+        o = torch.nn.functional.scaled_dot_product_attention(qr, kr, vt, attn_mask=mask,
+                                                             enable_gqa=(Hq != Hkv))
+        (o * torch.from_numpy(do)).sum().backward()
+        for a, t in ((dq, qt), (dk, kt), (dv, vt)):
+            assert np.allclose(a, t.grad.numpy(), atol=1e-12), np.max(np.abs(a - t.grad.numpy()))
+
+
+def check_backward_invariants(orc):
+    """Facts of the calculus that hold for any inputs:
+    - dO = 0 gives zero gradients;
+    - every probability row sums to one, so the dv rows of a KV head sum to the sum of dO
+      over all query rows of the heads that read it;
+    - without RoPE the output does not change when one vector is added to every key, so the
+      dk rows of a head sum to zero;
+    - with all keys equal every row attends uniformly whatever q is: dq = 0;
+    - a single key: O = v, so dq = dk = 0 and dv = the sum of dO over rows and heads."""
+    rng = _rng(32)
+    q, k, v, do = _bwd_case(rng, 1, 4, 2, 6, 8, 8)
+    for causal, base in ((False, 0.0), (True, 0.0), (True, 10000.0)):
+        z = orc.attention_backward(q, k, v, np.zeros_like(do), causal, base)
+        assert all(np.all(x == 0) for x in z)
+        dq, dk, dv = orc.attention_backward(q, k, v, do, causal, base)
+        for g in range(2):
+            assert np.allclose(dv[0, g].sum(axis=0), do[0, 2 * g:2 * g + 2].sum(axis=(0, 1)), atol=1e-12)
+        if base == 0.0:
+            assert np.allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    keq = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    dq, _, _ = orc.attention_backward(q, keq, v, do, False, 0.0)
+    assert np.allclose(dq, 0.0, atol=1e-12)
+    dq, dk, dv = orc.attention_backward(q, k[:, :, :1], v[:, :, :1], do, False, 10000.0)
+    assert np.allclose(dq, 0.0, atol=1e-12) and np.allclose(dk, 0.0, atol=1e-12)
+    assert np.allclose(dv[0, :, 0], do[0].reshape(2, 2, 6, 8).sum(axis=(1, 2)), atol=1e-12)
+
+
 ALL_CHECKS = [
+    check_backward_finite_differences, check_backward_torch_autograd, check_backward_invariants,
     check_prefill_paged_equals_contiguous,
     check_bruteforce_window,
     check_window_special_cases,

@@ -198,7 +198,44 @@ def m_window_off_by_one(mod):
     mod.window_mask = window_mask
 
 
-MUTATIONS = [m_window_off_by_one, m_mask_after_softmax, m_no_scale, m_scale_by_d, m_rope_freq_exponent, m_rope_clockwise,
+def _resource(mod, old, new):
+    """Re-execute the oracle's source with one substring replaced (must occur exactly once)."""
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) == 1, old
+    exec(compile(src.replace(old, new), ORACLE_SRC, "exec"), mod.__dict__)
+
+
+def m_bwd_missing_delta(mod):
+    """Softmax Jacobian without the rowsum(dO * O) term."""
+    _resource(mod, "ds = p * (dp - delta)", "ds = p * dp")
+
+
+def m_bwd_rope_forward_not_transpose(mod):
+    """Gradients rotated by +phi (the forward rotation) instead of its transpose."""
+    _resource(mod, "dq[b, h] = apply_rope_transpose(ds @ kr[b, g] * scale, qpos, rope_base)",
+              "dq[b, h] = apply_rope(ds @ kr[b, g] * scale, qpos, rope_base)")
+
+
+def m_bwd_gqa_overwrite(mod):
+    """The last query head of a group overwrites dv instead of adding to it."""
+    _resource(mod, "dv[b, g] += p.T @ do", "dv[b, g] = p.T @ do")
+
+
+def m_bwd_dk_unscaled(mod):
+    """dk without the 1/sqrt(d_h) of the scores."""
+    _resource(mod, "dk[b, g] += apply_rope_transpose(ds.T @ qr * scale, kpos, rope_base)",
+              "dk[b, g] += apply_rope_transpose(ds.T @ qr, kpos, rope_base)")
+
+
+def m_bwd_dk_uses_unrotated_q(mod):
+    """dk' formed from the unrotated queries."""
+    _resource(mod, "dk[b, g] += apply_rope_transpose(ds.T @ qr * scale, kpos, rope_base)",
+              "dk[b, g] += apply_rope_transpose(ds.T @ q[b, h] * scale, kpos, rope_base)")
+
+
+MUTATIONS = [m_bwd_missing_delta, m_bwd_rope_forward_not_transpose, m_bwd_gqa_overwrite,
+             m_bwd_dk_unscaled, m_bwd_dk_uses_unrotated_q,
+             m_window_off_by_one, m_mask_after_softmax, m_no_scale, m_scale_by_d, m_rope_freq_exponent, m_rope_clockwise,
              m_rope_rotate_half_pairs, m_rope_only_queries, m_gqa_modulo, m_causal_off_by_one,
              m_lse_without_max, m_pos_ignored, m_decode_position_L, m_gather_swapped,
              m_probs_transposed, m_no_max_subtraction_overflow]
