@@ -16,7 +16,8 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ER
 ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTED = ("attn_fwd", "attn_fwd_window", "attn_prefill_paged", "attn_decode_paged",
-            "attn_decode_workspace_bytes", "attn_paged_gather", "attn_status_str")
+            "attn_decode_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes", "attn_paged_gather",
+            "attn_status_str")
 
 
 def _load():
@@ -39,6 +40,11 @@ def _load():
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_paged_gather.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.attn_paged_gather.restype = i32
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, f32,
+                             i64, vp, sz, i32, vp]
+    lib.attn_bwd.restype = i32
+    lib.attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, f32]
+    lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_status_str.argtypes = [i32]
     lib.attn_status_str.restype = ctypes.c_char_p
     return lib
@@ -185,6 +191,34 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, block_size=16,
                                _dtype_code(q), _stream(stream))
     _check(st, "attn_decode_paged")
     return out, lse
+
+
+def attn_bwd_workspace_bytes(B, Hq, Hkv, T, S, d_h, rope_base=0.0):
+    return int(LIB.attn_bwd_workspace_bytes(B, Hq, Hkv, T, S, d_h, float(rope_base)))
+
+
+def attn_bwd(q, k, v, out, lse, dout, causal=False, window=0, rope_base=0.0, pos=0, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """Gradients of attention with respect to q, k, v given the forward's out and lse and the
+    output gradient dout.  Same shapes and options as the forward call (window > 0 means the
+    causal sliding window of attn_fwd_window).  Returns (dq, dk, dv)."""
+    import torch
+    _, _, (B, Hq, Hkv, T, S, d) = _fwd_buffers(q, k, v, out, lse, True)
+    _require(dout.shape == q.shape and dout.dtype == q.dtype and dout.is_cuda and dout.is_contiguous(), "bad dout")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        _require(t.shape == ref.shape and t.dtype == ref.dtype and t.is_contiguous(), "bad gradient buffer")
+    need = attn_bwd_workspace_bytes(B, Hq, Hkv, T, S, d, rope_base)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = LIB.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                      B, Hq, Hkv, T, S, d, int(bool(causal)), int(window), float(rope_base), int(pos),
+                      _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(q),
+                      _stream(stream))
+    _check(st, "attn_bwd")
+    return dq, dk, dv
 
 
 def attn_paged_gather(cache, block_table, seq_lens, block_size=16, dst=None, stream=None):

@@ -135,6 +135,80 @@ attn_status_t attn_prefill_paged(const void* q, const void* k_cache, const void*
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+bool bwd_sizes_ok(int B, int Hq, int Hkv, int T, int S, int d_h) {
+  return B >= 1 && Hq >= 1 && Hkv >= 1 && T >= 1 && S >= 1 && d_h >= 1 && Hq % Hkv == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int S, int d_h, float rope_base) {
+  if (!bwd_sizes_ok(B, Hq, Hkv, T, S, d_h) || bad_base(rope_base)) return 0;
+  const size_t rows = (size_t)B * Hq * T;
+  size_t n = 2 * align256(rows * sizeof(float));
+  if (rope_base > 0.f) n += align256(rows * d_h * 2) + align256((size_t)B * Hkv * S * d_h * 2);
+  return n;
+}
+
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int T, int S,
+                       int d_h, int causal, int64_t window, float rope_base, int64_t pos, void* workspace,
+                       size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
+  if (!bwd_sizes_ok(B, Hq, Hkv, T, S, d_h)) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (window < 0 || (window > 0 && causal != 1)) return ATTN_ERR_INVALID_ARG;
+  if (bad_base(rope_base)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16 || d_h != 128) return ATTN_ERR_UNSUPPORTED;
+  if (pos > ((int64_t)1 << 40) || pos < -((int64_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn_bwd_workspace_bytes(B, Hq, Hkv, T, S, d_h, rope_base);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (window > ((int64_t)1 << 41)) window = (int64_t)1 << 41;
+
+  attn::BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  const size_t rows = (size_t)B * Hq * T;
+  char* ws = (char*)workspace;
+  p.lse2 = (float*)ws;
+  ws += align256(rows * sizeof(float));
+  p.delta = (float*)ws;
+  ws += align256(rows * sizeof(float));
+  p.use_rope = rope_base > 0.f;
+  if (p.use_rope) {
+    p.qr = ws;
+    ws += align256(rows * d_h * 2);
+    p.kr = ws;
+  }
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.T = T;
+  p.S = S;
+  p.causal = causal;
+  p.window = window;
+  p.pos = pos;
+  fill_rope(p.rope_c, d_h, p.use_rope ? rope_base : 1.f);
+  hipError_t e = attn::launch_bwd_bf16(p, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_h, int max_blocks_per_seq,
                                    int block_size) {
   if (num_seqs < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d_h < 1 || max_blocks_per_seq < 1 ||

@@ -67,6 +67,14 @@ __device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, int voffset, void*
 #endif
 }
 
+// 4 bytes at byte offset voffset of a buffer straight into LDS: lane i writes
+// lds_wave_base + 4 * i.
+__device__ __forceinline__ void buffer_load_lds4(i32x4 rsrc, int voffset, void* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  llvm_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 4, voffset, 0, 0, 0);
+#endif
+}
+
 // sin and cos of 2*pi*rev for |rev| <= 0.5 (hardware v_sin/v_cos take revolutions).
 __device__ __forceinline__ void sincos_rev(float rev, float* s, float* c) {
   *s = __builtin_amdgcn_sinf(rev);

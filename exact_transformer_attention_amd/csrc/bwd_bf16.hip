@@ -1,0 +1,635 @@
+// bf16 exact attention backward on gfx950 matrix cores (fp32 accumulation).
+//
+// The backward pass recomputes the probabilities from the saved log-sum-exp instead of
+// reading a stored T x S matrix ("Why is attention O(n^2), how does FlashAttention
+// help ...", Deep dive: FlashAttention; "Self-Attention Complexity, FlashAttention,
+// PagedAttention, and RoPE in Code", Part 2).  With q', k' the rotated inputs,
+// S = q' k'^T / sqrt(d_h), P = softmax(S), O = P v and dO the incoming gradient:
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - rowsum(dO * O)),
+//     dq' = dS k' / sqrt(d_h),   dk' = dS^T q' / sqrt(d_h),
+// and RoPE being a rotation, dq and dk are dq', dk' rotated back by the same angles.
+//
+// Three kernels, all on the caller's stream:
+//  * preprocess: per query row, delta = rowsum(dO * O) and lse in base 2 (a row with no
+//    visible key gets +inf, so its probabilities recompute to 0); with RoPE, q and k are
+//    rotated once (angles reduced in fp64) into the workspace as bf16, so the two gradient
+//    kernels stream plain tiles.
+//  * dK/dV: a workgroup owns 128 keys of one KV head (four waves of 32).  It walks every
+//    query block of every query head that reads this KV head (grouped-query sums stay in
+//    registers; no atomics), streaming q' and dO tiles through LDS.  In the orientation
+//    S = q' k'^T a lane owns one key column, so P and dS leave the accumulators directly
+//    as the B operands of dV^T += dO^T P and dk'^T += q'^T dS (the contraction over queries
+//    is permuted to match the accumulator rows), and dO^T, q'^T are read with
+//    ds_read_b64_tr_b16.  The wave's own k' and V columns stay in registers.
+//  * dQ: shaped like the forward kernel.  Eight waves of 32 queries (the query heads of one
+//    KV head packed together) stream k' and V tiles; S^T = k' q'^T and dP^T = V dO^T put a
+//    query in each lane, and dq'^T += k'^T dS^T takes dS^T straight from the accumulators.
+// Probabilities and dS are rounded to bf16 for the products; everything else is fp32.
+// Tiles are stored with an xor swizzle of their 16-byte chunks that keeps both the row
+// reads (ds_read_b128) and the transposed reads free of bank conflicts.
+#include <math.h>
+
+#include <type_traits>
+
+#include "attn_common.h"
+#include "fwd_params.h"
+#include "launchers.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kCPR = kD / 8;   // 16-byte chunks per row
+constexpr int kKS = kD / 16;   // k-steps over the head dimension
+constexpr int kDB = kD / 32;   // 32-wide blocks of the head dimension
+constexpr int kRowBytes = kD * 2;
+constexpr int kTileRows = 64;  // rows of a streamed tile (queries in dK/dV, keys in dQ)
+constexpr int kTileChunks = kTileRows * kCPR;
+
+constexpr int kKVW = 4;                 // dK/dV: waves per workgroup
+constexpr int kKVThreads = kKVW * kWave;
+constexpr int kKeysPerWG = kKVW * 32;
+constexpr int kQW = 8;                  // dQ: waves per workgroup (two per SIMD)
+constexpr int kQThreads = kQW * kWave;
+
+// Chunk swizzle of tile row r (a 4-bit xor on the chunk index).  With a = r & 3 and
+// b = (r >> 2) & 3: bits 2-3 are a permutation of a and so are bits 1-2, so the four rows a
+// transposed read touches land in distinct 32- and 64-byte bank groups; over 16
+// consecutive rows the value is a permutation of 0..15, so 8 or 16 lanes reading the same
+// logical chunk of consecutive rows hit distinct banks.
+__device__ __forceinline__ int bswz(int r) {
+  const int a = r & 3, b = (r >> 2) & 3;
+  return (b & 1) | ((((a >> 1) ^ (b >> 1)) & 1) << 1) | ((a & 1) << 2) | ((a >> 1) << 3);
+}
+
+// Byte offset of logical chunk c of row r in a swizzled tile.
+__device__ __forceinline__ int tile_off(int r, int c) { return r * kRowBytes + ((c ^ bswz(r)) << 4); }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// Transposed A operand: lane l gets column (l % 32) of the 32-column block for the 16 rows
+// of one k-step, in the accumulator row order (rows 4g..4g+3 from the first address, rows
+// 8+4g..8+4g+3 from the second).
+__device__ __forceinline__ bf16x8 tr_read(const char* p0, const char* p1) {
+  const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+  const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
+  const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
+  return __builtin_bit_cast(bf16x8, (u32x4){w0[0], w0[1], w1[0], w1[1]});
+}
+
+// Per-lane offsets of the transposed reads of 32-column block db, rows 0..15 of a tile.
+__device__ __forceinline__ void tr_offsets(int lane, int (&t0)[kDB], int (&t1)[kDB]) {
+  const int g = lane / 32, a16 = lane / 16, lam = lane % 16;
+  const int r0 = 4 * g + lam / 4;
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) {
+    const int col = db * 32 + 16 * (a16 % 2) + 4 * (lam % 4);
+    const int c = col / 8, half = (col % 8) / 4;
+    t0[db] = tile_off(r0, c) + half * 8;
+    t1[db] = tile_off(r0 + 8, c) + half * 8;
+  }
+}
+
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// Rotate pair (x0, x1) back by the RoPE angle of `turns` (the transpose of the rotation).
+__device__ __forceinline__ void unrotate(float& x0, float& x1, float turns) {
+  float sn, cs;
+  sincos_rev(turns, &sn, &cs);
+  const float y0 = x0 * cs + x1 * sn, y1 = x1 * cs - x0 * sn;
+  x0 = y0;
+  x1 = y1;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- preprocess ----
+// Rows [0, nq) are query rows (b, h, t): delta, lse2 and (RoPE) the rotated q.  Rows
+// [nq, nq + nk) are key rows (b, kvh, s) to rotate (RoPE only).  16 lanes per row, 8
+// elements (4 pairs) per lane.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long nq, long long nk) {
+  const int sub = threadIdx.x % 16;
+  const long long nrows = nq + nk;
+  const long long stride = (long long)gridDim.x * 16;
+  for (long long row = ((long long)blockIdx.x * 256 + threadIdx.x) / 16; row < nrows; row += stride) {
+    if (row < nq) {
+      const size_t e0 = (size_t)row * kD + sub * 8;
+      if (p.use_rope) {
+        const int64_t ps = p.pos + (int64_t)(row % p.T);
+        const u32x4 raw = *(const u32x4*)((const __bf16*)p.q + e0);
+        u32x4 outv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float sn, cs;
+          sincos_rev(rope_turns(ps, p.rope_c[sub * 4 + e]), &sn, &cs);
+          const float x0 = bf16_lo(raw[e]), x1 = bf16_hi(raw[e]);
+          outv[e] = pack_bf16(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+        }
+        *(u32x4*)((__bf16*)p.qr + e0) = outv;
+      }
+      const u32x4 d = *(const u32x4*)((const __bf16*)p.dout + e0);
+      const u32x4 o = *(const u32x4*)((const __bf16*)p.out + e0);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc += bf16_lo(d[e]) * bf16_lo(o[e]) + bf16_hi(d[e]) * bf16_hi(o[e]);
+      acc += __shfl_xor(acc, 8);
+      acc += __shfl_xor(acc, 4);
+      acc += __shfl_xor(acc, 2);
+      acc += __shfl_xor(acc, 1);
+      if (sub == 0) {
+        p.delta[row] = acc;
+        const float l = p.lse[row];
+        p.lse2[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      }
+    } else {
+      const long long kr = row - nq;
+      const int64_t ps = kr % p.S;
+      const size_t e0 = (size_t)kr * kD + sub * 8;
+      const u32x4 raw = *(const u32x4*)((const __bf16*)p.k + e0);
+      u32x4 outv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float sn, cs;
+        sincos_rev(rope_turns(ps, p.rope_c[sub * 4 + e]), &sn, &cs);
+        const float x0 = bf16_lo(raw[e]), x1 = bf16_hi(raw[e]);
+        outv[e] = pack_bf16(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+      }
+      *(u32x4*)((__bf16*)p.kr + e0) = outv;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------- dK/dV ----
+__global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) u32x4 Qs[2][kTileChunks];  // q' tile, swizzled
+  __shared__ __attribute__((aligned(16))) u32x4 Os[2][kTileChunks];  // dO tile, swizzled
+  __shared__ __attribute__((aligned(16))) float Ls[2][kTileRows];    // lse2 of the tile rows
+  __shared__ __attribute__((aligned(16))) float Ds[2][kTileRows];    // delta of the tile rows
+
+  const int tid = threadIdx.x;
+  const int wid = tid / kWave;
+  const int lane = tid % kWave;
+  const int l32 = lane % 32;
+  const int g = lane / 32;
+
+  // ---- work item: (batch, KV head, 128-key block).  Key blocks run in increasing order
+  // (for causal attention the first blocks see the most queries); all blocks of one KV
+  // head stay on one XCD so its q' / dO tiles are shared through that XCD's L2.
+  int kb, grp;
+  {
+    const int bid = blockIdx.x;
+    if (p.xcd_remap) {
+      const int xcd = bid % 8, slot = bid / 8, gpx = p.n_groups / 8;
+      kb = slot / gpx;
+      grp = xcd + 8 * (slot % gpx);
+    } else {
+      kb = bid / p.n_groups;
+      grp = bid % p.n_groups;
+    }
+  }
+  const int b = grp / p.Hkv, kvh = grp % p.Hkv;
+  const int G = p.Hq / p.Hkv;
+  const int T = p.T, S = p.S;
+  const int64_t pos = p.pos;
+  const int kb0 = kb * kKeysPerWG;
+  const int kw0 = kb0 + wid * 32;  // first key of this wave
+  const int key = kw0 + l32;       // this lane's key column
+
+  const size_t kvrow0 = ((size_t)b * p.Hkv + kvh) * (size_t)S;
+  const __bf16* kg = (const __bf16*)(p.use_rope ? p.kr : p.k) + kvrow0 * kD;
+  const __bf16* vg = (const __bf16*)p.v + kvrow0 * kD;
+  const __bf16* qbase = (const __bf16*)(p.use_rope ? p.qr : p.q);
+  const __bf16* obase = (const __bf16*)p.dout;
+
+  // k'^T and V^T as B operands: lane holds key `key`, dims ks*16 + g*8 .. +7.
+  bf16x8 kop[kKS], vop[kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
+    if (key < S) {
+      kr = *(const u32x4*)(kg + (size_t)key * kD + ks * 16 + g * 8);
+      vr = *(const u32x4*)(vg + (size_t)key * kD + ks * 16 + g * 8);
+    }
+    kop[ks] = __builtin_bit_cast(bf16x8, kr);
+    vop[ks] = __builtin_bit_cast(bf16x8, vr);
+  }
+
+  // ---- queries that see at least one key of this block.
+  int64_t qlo = 0, qhi = T;
+  if (p.causal) qlo = (int64_t)kb0 - pos;  // key kb0 is visible from query kb0 - pos on
+  if (p.window > 0) {
+    const int64_t klast = (int64_t)min(kb0 + kKeysPerWG, S) - 1;
+    qhi = klast + p.window - pos;  // key klast is visible to queries below this
+  }
+  qlo = qlo < 0 ? 0 : (qlo > T ? T : qlo);
+  qhi = qhi > T ? T : qhi;
+  const int qb_lo = (int)(qlo / kTileRows);
+  const int nqb = qhi > qlo ? (int)((qhi + kTileRows - 1) / kTileRows) - qb_lo : 0;
+  const int n_it = G * nqb;
+
+  // ---- tile loads: this thread's chunks of rows row0 + 4j (direct to LDS, swizzled).
+  const int slot = lane % kCPR;
+  const int row0 = wid * 16 + lane / kCPR;
+  int goff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = row0 + 4 * j;
+    goff[j] = (r * kD + (slot ^ bswz(r)) * 8) * 2;
+  }
+  auto load_tile = [&](int it, auto bc) {
+    constexpr int BUF = decltype(bc)::value;
+    const int hh = it / nqb, qb = qb_lo + it % nqb;
+    const int q0 = qb * kTileRows;
+    const size_t rowbase = ((size_t)b * p.Hq + (size_t)kvh * G + hh) * (size_t)T + q0;
+    const uint32_t nrows = (uint32_t)min(T - q0, kTileRows);
+    const i32x4 rq = make_rsrc(qbase + rowbase * kD, nrows * kRowBytes);
+    const i32x4 ro = make_rsrc(obase + rowbase * kD, nrows * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) buffer_load_lds16(rq, goff[j], &Qs[BUF][(wid * 4 + j) * kWave]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) buffer_load_lds16(ro, goff[j], &Os[BUF][(wid * 4 + j) * kWave]);
+    if (wid == 0) buffer_load_lds4(make_rsrc(p.lse2 + rowbase, nrows * 4), lane * 4, &Ls[BUF][0]);
+    if (wid == 1) buffer_load_lds4(make_rsrc(p.delta + rowbase, nrows * 4), lane * 4, &Ds[BUF][0]);
+  };
+
+  int noff[kKS];  // row reads: row l32, chunk ks*2 + g
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) noff[ks] = tile_off(l32, ks * 2 + g);
+  int toff0[kDB], toff1[kDB];
+  tr_offsets(lane, toff0, toff1);
+
+  f32x16 dv[kDB], dk[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) {
+    dv[db] = zero16();
+    dk[db] = zero16();
+  }
+  const float c2 = kLog2e / sqrtf((float)kD);
+
+  auto compute = [&](int it, auto bc) {
+    constexpr int BUF = decltype(bc)::value;
+    const int qb = qb_lo + it % nqb;
+    const char* qt = (const char*)&Qs[BUF][0];
+    const char* ot = (const char*)&Os[BUF][0];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int i0 = qb * kTileRows + mi * 32;  // first query of this 32 x 32 tile
+      bool vis = i0 < T && kw0 < S;
+      if (p.causal) vis = vis && (int64_t)kw0 <= pos + i0 + 31;
+      if (p.window > 0) vis = vis && (int64_t)(kw0 + 31) > pos + i0 - p.window;
+      if (!vis) continue;
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const bf16x8 aq = *(const bf16x8*)(qt + noff[ks] + mi * 32 * kRowBytes);
+        const bf16x8 ao = *(const bf16x8*)(ot + noff[ks] + mi * 32 * kRowBytes);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kop[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vop[ks], dp, 0, 0, 0);
+      }
+      // statistics of this lane's 16 rows: rows mi*32 + q*8 + g*4 + (0..3)
+      f32x4 lr[4], dr[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lr[q] = *(const f32x4*)&Ls[BUF][mi * 32 + q * 8 + g * 4];
+        dr[q] = *(const f32x4*)&Ds[BUF][mi * 32 + q * 8 + g * 4];
+      }
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(s[r], c2, -lr[r / 4][r % 4]));
+      const bool need_mask = (p.causal && (int64_t)(kw0 + 31) > pos + i0) ||
+                             (p.window > 0 && (int64_t)kw0 <= pos + i0 + 31 - p.window);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t lim = pos + i0 + (r / 4) * 8 + g * 4 + (r % 4);  // last key this row sees
+          const bool ok = (int64_t)key <= lim && (p.window <= 0 || (int64_t)key > lim - p.window);
+          if (!ok) pr[r] = 0.f;
+        }
+      }
+      bf16x8 pb[2], db2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 pk, dk4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * h + 2 * e;
+          pk[e] = pack_bf16(pr[r], pr[r + 1]);
+          dk4[e] = pack_bf16(pr[r] * (dp[r] - dr[r / 4][r % 4]), pr[r + 1] * (dp[r + 1] - dr[r / 4][(r + 1) % 4]));
+        }
+        pb[h] = __builtin_bit_cast(bf16x8, pk);
+        db2[h] = __builtin_bit_cast(bf16x8, dk4);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rb = (mi * 2 + h) * 16 * kRowBytes;  // rows of this 16-query k-step
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const bf16x8 ao = tr_read(ot + rb + toff0[db], ot + rb + toff1[db]);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[h], dv[db], 0, 0, 0);
+          const bf16x8 aq = tr_read(qt + rb + toff0[db], qt + rb + toff1[db]);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, db2[h], dk[db], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Tile it lives in buffer it & 1 (a compile-time constant in each step, so the compiler
+  // can tell the buffer being filled from the one being read).
+  auto step = [&](auto bc, int it) {
+    constexpr int BUF = decltype(bc)::value;
+    __syncthreads();  // tile it has landed; everyone is done with tile it-1
+    if (it + 1 < n_it) load_tile(it + 1, std::integral_constant<int, BUF ^ 1>{});
+    compute(it, bc);
+    wait_loads();
+  };
+  if (n_it > 0) {
+    load_tile(0, std::integral_constant<int, 0>{});
+    wait_loads();
+  }
+  for (int it = 0; it < n_it; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_it) step(std::integral_constant<int, 1>{}, it + 1);
+  }
+
+  // ---- epilogue: dV, and dk = R^T dk' with dk' = dk'^T / sqrt(d_h) (pairs are in-lane).
+  if (key < S) {
+    __bf16* dvg = (__bf16*)p.dv + (kvrow0 + key) * kD;
+    __bf16* dkg = (__bf16*)p.dk + (kvrow0 + key) * kD;
+    const float isd = 1.f / sqrtf((float)kD);
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + q4 * 8 + g * 4;
+        u32x2 w;
+        w[0] = pack_bf16(dv[db][4 * q4 + 0], dv[db][4 * q4 + 1]);
+        w[1] = pack_bf16(dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]);
+        *(u32x2*)(dvg + d0) = w;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = dk[db][4 * q4 + e] * isd;
+        if (p.use_rope) {
+          unrotate(x[0], x[1], rope_turns((int64_t)key, p.rope_c[d0 / 2]));
+          unrotate(x[2], x[3], rope_turns((int64_t)key, p.rope_c[d0 / 2 + 1]));
+        }
+        w[0] = pack_bf16(x[0], x[1]);
+        w[1] = pack_bf16(x[2], x[3]);
+        *(u32x2*)(dkg + d0) = w;
+      }
+  }
+}
+
+// ------------------------------------------------------------------------- dQ ----
+template <int HP>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(kQW / 4, kQW / 4)))
+void bwd_dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) u32x4 Ks[2][kTileChunks];  // k' tile, swizzled
+  __shared__ __attribute__((aligned(16))) u32x4 Vs[2][kTileChunks];  // V tile, swizzled
+
+  const int tid = threadIdx.x;
+  const int wid = tid / kWave;
+  const int lane = tid % kWave;
+  const int l32 = lane % 32;
+  const int g = lane / 32;
+
+  // ---- work item: (batch, head group, query block), longest causal blocks first, all
+  // blocks of one head group on one XCD.
+  constexpr int RH = kQW * 32 / HP;  // rows per head per workgroup
+  int qb, grp;
+  {
+    const int bid = blockIdx.x;
+    if (p.xcd_remap) {
+      const int xcd = bid % 8, slot = bid / 8, gpx = p.n_groups / 8;
+      qb = p.n_qblocks - 1 - slot / gpx;
+      grp = xcd + 8 * (slot % gpx);
+    } else {
+      qb = p.n_qblocks - 1 - bid / p.n_groups;
+      grp = bid % p.n_groups;
+    }
+  }
+  const int hpg = p.Hq / HP;
+  const int b = grp / hpg;
+  const int hq = (grp % hpg) * HP + wid / (kQW / HP);
+  const int kvh = ((grp % hpg) * HP) / (p.Hq / p.Hkv);
+  const int T = p.T, S = p.S;
+  const int64_t pos = p.pos;
+  const int wrow0 = qb * RH + (wid % (kQW / HP)) * 32;  // first query row of this wave
+  const int t = wrow0 + l32;                            // this lane's query
+
+  const size_t row = ((size_t)b * p.Hq + hq) * (size_t)T + t;
+  const __bf16* qg = (const __bf16*)(p.use_rope ? p.qr : p.q);
+  const __bf16* og = (const __bf16*)p.dout;
+  const size_t kvrow0 = ((size_t)b * p.Hkv + kvh) * (size_t)S;
+  const __bf16* kg = (const __bf16*)(p.use_rope ? p.kr : p.k) + kvrow0 * kD;
+  const __bf16* vg = (const __bf16*)p.v + kvrow0 * kD;
+
+  // q'^T and dO^T as B operands: lane holds query t, dims ks*16 + g*8 .. +7.
+  bf16x8 qop[kKS], dop[kKS];
+  float lse2 = INFINITY, delta = 0.f;  // rows past T: probabilities 0
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    u32x4 qr = {0u, 0u, 0u, 0u}, orw = {0u, 0u, 0u, 0u};
+    if (t < T) {
+      qr = *(const u32x4*)(qg + row * kD + ks * 16 + g * 8);
+      orw = *(const u32x4*)(og + row * kD + ks * 16 + g * 8);
+    }
+    qop[ks] = __builtin_bit_cast(bf16x8, qr);
+    dop[ks] = __builtin_bit_cast(bf16x8, orw);
+  }
+  if (t < T) {
+    lse2 = p.lse2[row];
+    delta = p.delta[row];
+  }
+
+  // ---- keys visible to this wave / to the workgroup (as in the forward kernel).
+  int nk_wave = S, nk_wg = S;
+  if (p.causal) {
+    const int64_t lw = pos + (int64_t)min(T - 1, wrow0 + 31) + 1;
+    nk_wave = (int)(lw < 0 ? 0 : (lw < S ? lw : S));
+    const int64_t lg = pos + (int64_t)min(T - 1, qb * RH + RH - 1) + 1;
+    nk_wg = (int)(lg < 0 ? 0 : (lg < S ? lg : S));
+  }
+  const int n_tiles = (nk_wg + kTileRows - 1) / kTileRows;
+  int64_t lo_wave = 0;
+  int it0 = 0;
+  if (p.window > 0) {
+    lo_wave = pos + wrow0 - p.window + 1;
+    const int64_t lo_wg = pos + (int64_t)qb * RH - p.window + 1;
+    it0 = (int)(lo_wg <= 0 ? 0 : (lo_wg < nk_wg ? lo_wg : nk_wg)) / kTileRows;
+  }
+
+  // ---- tile loads: 2 chunks per thread per tensor, rows row0 + 4j.
+  const int slot = lane % kCPR;
+  const int row0 = wid * 8 + lane / kCPR;
+  int goff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = row0 + 4 * j;
+    goff[j] = (r * kD + (slot ^ bswz(r)) * 8) * 2;
+  }
+  auto load_tile = [&](int tile, auto bc) {
+    constexpr int BUF = decltype(bc)::value;
+    const int k0 = tile * kTileRows;
+    const uint32_t nrows = (uint32_t)min(S - k0, kTileRows);
+    const i32x4 rk = make_rsrc(kg + (size_t)k0 * kD, nrows * kRowBytes);
+    const i32x4 rv = make_rsrc(vg + (size_t)k0 * kD, nrows * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) buffer_load_lds16(rk, goff[j], &Ks[BUF][(wid * 2 + j) * kWave]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) buffer_load_lds16(rv, goff[j], &Vs[BUF][(wid * 2 + j) * kWave]);
+  };
+
+  int noff[kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) noff[ks] = tile_off(l32, ks * 2 + g);
+  int toff0[kDB], toff1[kDB];
+  tr_offsets(lane, toff0, toff1);
+
+  f32x16 dq[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) dq[db] = zero16();
+  const float c2 = kLog2e / sqrtf((float)kD);
+
+  auto compute = [&](int tile, auto bc) {
+    constexpr int BUF = decltype(bc)::value;
+    const int k0 = tile * kTileRows;
+    if (!(k0 < nk_wave && (int64_t)(k0 + kTileRows) > lo_wave)) return;
+    const char* kt = (const char*)&Ks[BUF][0];
+    const char* vt = (const char*)&Vs[BUF][0];
+    const bool need_mask = (k0 + kTileRows > S) || (p.causal && (int64_t)(k0 + kTileRows - 1) > pos + wrow0) ||
+                           (p.window > 0 && (int64_t)k0 < lo_wave + 31);
+    const int64_t lim = pos + t;  // last key this lane's query sees
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      bf16x8 dsb[2];
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const bf16x8 ak = *(const bf16x8*)(kt + noff[ks] + mb * 32 * kRowBytes);
+        const bf16x8 av = *(const bf16x8*)(vt + noff[ks] + mb * 32 * kRowBytes);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qop[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dop[ks], dp, 0, 0, 0);
+      }
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(s[r], c2, -lse2));
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = k0 + mb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
+          const bool ok = kk < S && (!p.causal || (int64_t)kk <= lim) && (p.window <= 0 || (int64_t)kk > lim - p.window);
+          if (!ok) pr[r] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * h + 2 * e;
+          pk[e] = pack_bf16(pr[r] * (dp[r] - delta), pr[r + 1] * (dp[r + 1] - delta));
+        }
+        dsb[h] = __builtin_bit_cast(bf16x8, pk);
+      }
+      // dq'^T += k'^T dS^T over this half's two 16-key steps
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rb = (mb * 2 + h) * 16 * kRowBytes;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const bf16x8 ak = tr_read(kt + rb + toff0[db], kt + rb + toff1[db]);
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, dsb[h], dq[db], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  auto step = [&](auto bc, int tile) {
+    constexpr int BUF = decltype(bc)::value;
+    __syncthreads();
+    if (tile + 1 < n_tiles) load_tile(tile + 1, std::integral_constant<int, BUF ^ 1>{});
+    compute(tile, bc);
+    wait_loads();
+  };
+  if (it0 < n_tiles) {
+    if (it0 & 1) load_tile(it0, std::integral_constant<int, 1>{});
+    else load_tile(it0, std::integral_constant<int, 0>{});
+    wait_loads();
+  }
+  int it = it0;
+  if (it < n_tiles && (it & 1)) step(std::integral_constant<int, 1>{}, it++);
+  for (; it < n_tiles; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1);
+  }
+
+  // ---- epilogue: dq = R^T dq' with dq' = dq'^T / sqrt(d_h).
+  if (t < T) {
+    __bf16* dqg = (__bf16*)p.dq + row * kD;
+    const float isd = 1.f / sqrtf((float)kD);
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + q4 * 8 + g * 4;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = dq[db][4 * q4 + e] * isd;
+        if (p.use_rope) {
+          unrotate(x[0], x[1], rope_turns(pos + t, p.rope_c[d0 / 2]));
+          unrotate(x[2], x[3], rope_turns(pos + t, p.rope_c[d0 / 2 + 1]));
+        }
+        u32x2 w;
+        w[0] = pack_bf16(x[0], x[1]);
+        w[1] = pack_bf16(x[2], x[3]);
+        *(u32x2*)(dqg + d0) = w;
+      }
+  }
+}
+
+namespace {
+template <int HP>
+hipError_t launch_dq(BwdParams p, hipStream_t stream) {
+  constexpr int RH = kQW * 32 / HP;
+  p.n_qblocks = (p.T + RH - 1) / RH;
+  p.n_groups = p.B * (p.Hq / HP);
+  p.xcd_remap = (p.n_groups % 8) == 0;
+  const long long grid = (long long)p.n_qblocks * p.n_groups;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_dq_kernel<HP>), dim3((unsigned)grid), dim3(kQThreads), 0, stream, p);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_bwd_bf16(BwdParams p, hipStream_t stream) {
+  const long long nq = (long long)p.B * p.Hq * p.T;
+  const long long nk = p.use_rope ? (long long)p.B * p.Hkv * p.S : 0;
+  long long grid = (nq + nk + 15) / 16;
+  if (grid > 16384) grid = 16384;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p, nq, nk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  BwdParams kv = p;
+  kv.n_kblocks = (p.S + kKeysPerWG - 1) / kKeysPerWG;
+  kv.n_groups = p.B * p.Hkv;
+  kv.xcd_remap = (kv.n_groups % 8) == 0;
+  grid = (long long)kv.n_kblocks * kv.n_groups;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)grid), dim3(kKVThreads), 0, stream, kv);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int G = p.Hq / p.Hkv;
+  if (G % 4 == 0) return launch_dq<4>(p, stream);
+  if (G % 2 == 0) return launch_dq<2>(p, stream);
+  return launch_dq<1>(p, stream);
+}
+
+}  // namespace attn

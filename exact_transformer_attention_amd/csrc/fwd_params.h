@@ -33,4 +33,29 @@ struct FwdParams {
   double rope_c[kMaxHalfDim];
 };
 
+// Backward pass (bf16, d_h = 128).  The workspace holds the per-row statistics and, with
+// RoPE, the rotated q and k that both gradient kernels read.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* lse2;      // [B, Hq, T] lse * log2(e); +inf for rows with no visible key
+  float* delta;     // [B, Hq, T] rowsum(dout * out)
+  void* qr;         // [B, Hq, T, d_h] bf16 rotated q (RoPE), else null
+  void* kr;         // [B, Hkv, S, d_h] bf16 rotated k (RoPE), else null
+  int B, Hq, Hkv, T, S;
+  int causal;
+  int use_rope;
+  int64_t window;   // > 0: causal sliding window, as in FwdParams
+  int64_t pos;
+  int n_qblocks, n_kblocks, n_groups, xcd_remap;
+  double rope_c[kMaxHalfDim];
+};
+
 }  // namespace attn

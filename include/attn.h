@@ -33,7 +33,7 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1,  /* NULL pointer, non-positive size, Hq % Hkv != 0, bad table size */
   ATTN_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (d_h, dtype, block_size) */
-  ATTN_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than attn_decode_workspace_bytes() */
+  ATTN_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than the *_workspace_bytes() size */
   ATTN_ERR_HIP = 4           /* the HIP runtime rejected a launch */
 } attn_status_t;
 
@@ -153,6 +153,38 @@ ATTN_API attn_status_t attn_prefill_paged(const void* q, const void* k_cache, co
                                           int T, int max_blocks_per_seq, int num_blocks,
                                           float rope_base, void* out, float* lse, attn_dtype_t dtype,
                                           void* stream);
+
+/*
+ * attn_bwd -- gradients of exact attention (as computed by attn_fwd / attn_fwd_window)
+ * with respect to q, k and v.  The probabilities are recomputed from the forward's saved
+ * lse instead of being stored ("Why is attention O(n^2), how does FlashAttention help
+ * ...", Deep dive: FlashAttention; "Self-Attention Complexity, FlashAttention,
+ * PagedAttention, and RoPE in Code", Part 2); the gradients themselves follow from the
+ * chain rule: dV = P^T dO, dS = P * (dO V^T - rowsum(dO * O)), dq' = dS k' / sqrt(d_h),
+ * dk' = dS^T q' / sqrt(d_h), with q', k' the rotated inputs and dq, dk rotated back.
+ *
+ *   q, k, v, causal, window, rope_base, pos   as given to the forward call (window 0: no
+ *            window; window >= 1 requires causal = 1)
+ *   out      [B, Hq, T, d_h] the forward's output;  lse [B, Hq, T] fp32 the forward's lse
+ *   dout     [B, Hq, T, d_h] gradient of the loss with respect to out
+ *   dq       [B, Hq, T, d_h];  dk, dv [B, Hkv, S, d_h]: results (dtype of the inputs).  With
+ *            grouped-query attention dk and dv of a KV head sum over the query heads that
+ *            read it.  Keys no query sees get zero gradients.
+ *   workspace  device scratch of at least attn_bwd_workspace_bytes(...) bytes (per-row
+ *            statistics and, with RoPE, the rotated q and k); caller-owned, no clearing
+ *            needed; overlapping calls must not share one workspace
+ * Supported: bf16, d_h == 128 (ATTN_ERR_UNSUPPORTED otherwise).  Three kernels are
+ * enqueued on `stream`; results are deterministic (no atomics).
+ */
+ATTN_API attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                int B, int Hq, int Hkv, int T, int S, int d_h, int causal,
+                                int64_t window, float rope_base, int64_t pos, void* workspace,
+                                size_t workspace_bytes, attn_dtype_t dtype, void* stream);
+
+/* Bytes of workspace attn_bwd needs for these sizes (0 on invalid sizes). */
+ATTN_API size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int S, int d_h,
+                                         float rope_base);
 
 /* Bytes of workspace attn_decode_paged needs for these sizes (0 on invalid sizes). */
 ATTN_API size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_h,

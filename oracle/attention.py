@@ -279,6 +279,48 @@ def attention_backward(q, k, v, dout, causal=False, rope_base=0.0, pos=0, window
     return dq, dk, dv
 
 
+def attention_backward_sampled(q, k, v, dout, b, g, keys, rows, causal=False, rope_base=0.0, pos=0, window=0):
+    """Selected entries of attention_backward for one batch index b and one KV head g:
+    dk and dv at key positions `keys` (summed over the query heads that read g), and dq at
+    (h, t) pairs `rows` (h among those heads).  The same chain rule as attention_backward,
+    evaluated only for the requested rows and columns of the probability matrix of each
+    query head of the group; used to check full-size results entry by entry.
+    Returns (dq [len(rows), d_h], dk [len(keys), d_h], dv [len(keys), d_h]) in float64."""
+    q = np.asarray(q)
+    Hq, T, d_h = q.shape[1], q.shape[2], q.shape[3]
+    Hkv, S = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    keys = np.asarray(keys, dtype=np.int64)
+    qpos = pos + np.arange(T, dtype=np.int64)
+    kpos = np.arange(S, dtype=np.int64)
+    kr = apply_rope(np.asarray(k[b, g], dtype=F64), kpos, rope_base)
+    vg = np.asarray(v[b, g], dtype=F64)
+    mask = _mask(qpos, kpos, causal, window)
+    scale = 1.0 / np.sqrt(F64(d_h))
+    dq = np.zeros((len(rows), d_h))
+    dk = np.zeros((len(keys), d_h))
+    dv = np.zeros((len(keys), d_h))
+    for h in range(g * G, (g + 1) * G):
+        qr = apply_rope(np.asarray(q[b, h], dtype=F64), qpos, rope_base)
+        o, _, p = sdpa(qr, kr, vg, mask)
+        do = np.asarray(dout[b, h], dtype=F64)
+        delta = np.sum(do * o, axis=-1, keepdims=True)
+        # columns `keys` of P and dS
+        ds_cols = p[:, keys] * (do @ vg[keys].T - delta)
+        dv += p[:, keys].T @ do
+        dk += ds_cols.T @ qr * scale
+        for n, (hh, t) in enumerate(rows):
+            if hh != h:
+                continue
+            ds_row = p[t] * (vg @ do[t] - delta[t])
+            dq[n] = ds_row @ kr * scale
+        del p
+    dk = apply_rope_transpose(dk, keys, rope_base)
+    for n, (hh, t) in enumerate(rows):
+        dq[n] = apply_rope_transpose(dq[n][None], [pos + t], rope_base)[0]
+    return dq, dk, dv
+
+
 # ------------------------------------------------------------- decode ----
 
 def prefill_paged(q, k_cache, v_cache, block_table, seq_lens, block_size, rope_base=0.0, heads=None):

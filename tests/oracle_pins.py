@@ -642,8 +642,23 @@ def check_backward_invariants(orc):
     assert np.allclose(dv[0, :, 0], do[0].reshape(2, 2, 6, 8).sum(axis=(1, 2)), atol=1e-12)
 
 
+def check_backward_sampled_equals_full(orc):
+    """The sampled backward (used at full size) returns exactly the corresponding entries of
+    the full backward: keys and rows spread over the sequence, grouped heads, RoPE, causal,
+    windowed and non-causal cases."""
+    rng = _rng(33)
+    q, k, v, do = _bwd_case(rng, 2, 4, 2, 20, 30, 16)
+    keys = [0, 3, 29, 15]
+    rows = [(2, 0), (3, 19), (2, 7)]
+    for causal, w, pos in ((True, 0, 10), (False, 0, 0), (True, 7, 10)):
+        dq, dk, dv = orc.attention_backward(q, k, v, do, causal, 1e4, pos, w)
+        a, b_, c = orc.attention_backward_sampled(q, k, v, do, 1, 1, keys, rows, causal, 1e4, pos, w)
+        assert np.allclose(a, np.array([dq[1, h, t] for h, t in rows]), atol=1e-13)
+        assert np.allclose(b_, dk[1, 1, keys], atol=1e-13) and np.allclose(c, dv[1, 1, keys], atol=1e-13)
+
+
 ALL_CHECKS = [
-    check_backward_finite_differences, check_backward_torch_autograd, check_backward_invariants,
+    check_backward_finite_differences, check_backward_sampled_equals_full, check_backward_torch_autograd, check_backward_invariants,
     check_prefill_paged_equals_contiguous,
     check_bruteforce_window,
     check_window_special_cases,

@@ -25,7 +25,8 @@ def lib():
 def test_header_declares_entry_points():
     names = header_functions()
     assert names == sorted(["attn_fwd", "attn_fwd_window", "attn_prefill_paged", "attn_decode_paged",
-                            "attn_decode_workspace_bytes", "attn_paged_gather", "attn_status_str"])
+                            "attn_decode_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes",
+                            "attn_paged_gather", "attn_status_str"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -121,6 +122,40 @@ def prefill_paged(lib, **kw):
 ])
 def test_prefill_paged_validation(lib, kw, status):
     assert prefill_paged(lib, **kw) == status
+
+
+def bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=4, Hkv=2, T=8,
+             S=8, d=128, causal=1, window=0, base=10000.0, pos=0, ws=FAKE, wsb=1 << 30, dtype=1)
+    a.update(kw)
+    return lib.attn_bwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["B"],
+                        a["Hq"], a["Hkv"], a["T"], a["S"], a["d"], a["causal"], a["window"], a["base"], a["pos"],
+                        a["ws"], a["wsb"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1),
+    (dict(dk=None), 1), (dict(dv=None), 1), (dict(B=0), 1), (dict(T=0), 1), (dict(S=0), 1), (dict(Hq=6, Hkv=4), 1),
+    (dict(causal=3), 1), (dict(window=-1), 1), (dict(window=5, causal=0), 1), (dict(base=-1.0), 1),
+    (dict(dtype=3), 1),
+    (dict(dtype=0), 2), (dict(d=64), 2), (dict(pos=1 << 41), 2),
+    (dict(ws=None), 3), (dict(wsb=100), 3),
+])
+def test_bwd_validation(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_bwd_workspace_bytes(lib):
+    import exact_transformer_attention_amd as e
+    # two fp32 per query row (lse in base 2, rowsum(dO * O)), each array 256-byte aligned;
+    # with RoPE also the rotated q and k in bf16
+    rows = 2 * 32 * 8192
+    assert e.attn_bwd_workspace_bytes(2, 32, 8, 8192, 8192, 128, 0.0) == 2 * rows * 4
+    assert e.attn_bwd_workspace_bytes(2, 32, 8, 8192, 8192, 128, 1e4) == 2 * rows * 4 + rows * 256 + 2 * 8 * 8192 * 256
+    assert e.attn_bwd_workspace_bytes(1, 1, 1, 3, 5, 128, 0.0) == 2 * 256
+    assert e.attn_bwd_workspace_bytes(1, 1, 1, 3, 5, 128, 1e4) == 2 * 256 + 768 + 1280
+    assert e.attn_bwd_workspace_bytes(1, 6, 4, 3, 5, 128, 0.0) == 0
+    assert e.attn_bwd_workspace_bytes(1, 1, 1, 3, 5, 128, -1.0) == 0
 
 
 def test_workspace_bytes(lib):

@@ -65,6 +65,18 @@ def make_fwd_inputs(B, Hq, Hkv, T, S, d_h, dtype="bf16", sigma=1.0, seed=0, **_)
     return q, k, v
 
 
+def make_bwd_inputs(B, Hq, Hkv, T, S, d_h, dtype="bf16", sigma=1.0, seed=0, **_):
+    """Q, K, V as make_fwd_inputs (same seed, same draws) followed by the output gradient
+    dO [B,Hq,T,d_h] iid N(0, 1) from the same generator, rounded to dtype."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    td = _TORCH_DTYPE[dtype]
+    q = (torch.randn((B, Hq, T, d_h), generator=g, dtype=torch.float32) * sigma).to(td)
+    k = (torch.randn((B, Hkv, S, d_h), generator=g, dtype=torch.float32) * sigma).to(td)
+    v = (torch.randn((B, Hkv, S, d_h), generator=g, dtype=torch.float32) * sigma).to(td)
+    do = torch.randn((B, Hq, T, d_h), generator=g, dtype=torch.float32).to(td)
+    return q, k, v, do
+
+
 def make_decode_inputs(num_seqs, Hq, Hkv, d_h, block_size=16, len_lo=512, len_hi=8192,
                        dtype="bf16", sigma=1.0, seed=0, seq_lens=None, device=None, **_):
     """Paged KV cache for one decode step.
@@ -167,6 +179,13 @@ def prefill_paged_flops(seq_lens, Hq, T, d_h):
 def fwd_flops(B, Hq, T, S, d_h, causal, **_):
     """Algorithmic FLOPs of one forward: 4*B*Hq*T*S*d_h, halved when causal."""
     f = 4.0 * B * Hq * T * S * d_h
+    return f / 2.0 if causal else f
+
+
+def bwd_flops(B, Hq, T, S, d_h, causal, **_):
+    """Algorithmic FLOPs of one backward: the five T x S x d_h products (S recomputed, dP,
+    dV, dQ, dK), 10*B*Hq*T*S*d_h, halved when causal (2.5 times the forward)."""
+    f = 10.0 * B * Hq * T * S * d_h
     return f / 2.0 if causal else f
 
 
