@@ -97,7 +97,9 @@ def summarize_pmc(fetch_csv, write_csv, out_dir, extra_kind=None):
     w_scale = copy_bytes / w_copy if w_copy else 1.0
     res = {"calibration": {"kernel": "1 GiB device copy", "fetch_raw_bytes": f_copy, "write_raw_bytes": w_copy,
                            "fetch_scale": f_scale, "write_scale": w_scale}}
-    kinds = (((extra_kind, ["fwd_bf16_kernel"], PREFILL_SOURCES),) if extra_kind else
+    kinds = (((extra_kind, ["bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"], BWD_SOURCES),)
+             if extra_kind == "bwd" else
+             ((extra_kind, ["fwd_bf16_kernel"], PREFILL_SOURCES),) if extra_kind else
              (("prefill", ["fwd_bf16_kernel"], PREFILL_SOURCES),
               ("decode", ["decode_partial_kernel", "decode_merge_kernel"], DECODE_SOURCES)))
     path = os.path.join(out_dir, "traffic.json")
@@ -309,6 +311,81 @@ def prefix_bench(a):
     print(json.dumps(res), flush=True)
 
 
+BWD_SOURCES = ["exact_transformer_attention_amd/csrc/bwd_bf16.hip",
+               "exact_transformer_attention_amd/csrc/attn_common.h",
+               "exact_transformer_attention_amd/csrc/fwd_params.h"]
+
+
+def bwd_bench(a):
+    """Backward (attn_bwd: preprocess + dK/dV + dQ kernels) of the causal 8192-token GQA
+    workload, given the forward's out and lse (one JSON line)."""
+    import torch
+    import workloads
+    from exact_transformer_attention_amd import attn_bwd, attn_bwd_workspace_bytes, attn_fwd
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS["gqa8k"]
+    q, k, v, do = (t.to(dev) for t in workloads.make_bwd_inputs(**cfg))
+    out, lse = attn_fwd(q, k, v, causal=True, rope_base=cfg["rope_base"], pos=cfg["pos"])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(attn_bwd_workspace_bytes(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], cfg["S"], cfg["d_h"],
+                                              cfg["rope_base"]), dtype=torch.uint8, device=dev)
+
+    def run():
+        attn_bwd(q, k, v, out, lse, do, causal=True, rope_base=cfg["rope_base"], pos=cfg["pos"], dq=dq, dk=dk,
+                 dv=dv, workspace=ws)
+
+    for _ in range(a.warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    avg = sum(ms) / len(ms)
+    assert all(bool(torch.isfinite(t).all()) for t in (dq, dk, dv))
+    if a.copy_calibration:
+        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+    flops = workloads.bwd_flops(**cfg)
+    tf = flops / (avg * 1e-3) / 1e12
+    res = {
+        "metric": "attention bwd TFLOP/s + % bf16 MFMA peak",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(avg, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded iid normal, bf16-rounded)",
+        "config": {"workload": "backward of causal GQA prefill B=2 Hq=32 Hkv=8 T=S=8192 d_h=128 RoPE 1e4 "
+                               "(dq, dk, dv from out, lse and dO)"},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("bwd", kernel_sources_digest(BWD_SOURCES)),
+                     "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel<4>", "flop_per_launch": flops,
+                     "avg_launch_ms": round(avg, 4)},
+    }
+    if not a.no_cpu_baseline:
+        import oracle
+        print("[bench] timing the oracle on the host (backward sample)", file=sys.stderr, flush=True)
+        qh, kh, vh, doh = workloads.make_bwd_inputs(**cfg)
+        nq = cfg["Hq"] // cfg["Hkv"]
+        t0 = time.perf_counter()
+        oracle.attention_backward(qh[:1, :nq].double().numpy(), kh[:1, :1].double().numpy(),
+                                  vh[:1, :1].double().numpy(), doh[:1, :nq].double().numpy(), True,
+                                  cfg["rope_base"], cfg["pos"])
+        dt = time.perf_counter() - t0
+        sf = workloads.bwd_flops(1, nq, cfg["T"], cfg["S"], cfg["d_h"], True)
+        res["cpu_baseline"] = dict(value=sf / dt / 1e12, unit="TFLOP/s", cores=cpu_threads(), kind="oracle",
+                                   seconds=round(dt, 3),
+                                   sample=f"batch 0, KV head 0 and its {nq} query heads, all {cfg['T']} rows, "
+                                          f"fp64 numpy; {sf:.3e} algorithmic FLOP")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,10 +394,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "decode", "window", "prefix"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "window", "prefix", "bwd"], default=None,
                     help="time only one part (profiling runs); 'window' times the causal sliding-window "
                          "prefill (attn_fwd_window) on the same 8192-token GQA workload instead; 'prefix' "
-                         "the paged prefill (attn_prefill_paged) of 8 sequences over a shared 6144-token prefix")
+                         "the paged prefill (attn_prefill_paged) of 8 sequences over a shared 6144-token prefix; "
+                         "'bwd' the backward (attn_bwd) of the 8192-token GQA prefill")
     ap.add_argument("--window", type=int, default=4096, help="window of --only window (keys)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/traffic.json "
@@ -328,7 +406,7 @@ def main():
     a = ap.parse_args()
     if a.traffic_from:
         print(json.dumps(summarize_pmc(a.traffic_from[0], a.traffic_from[1], os.path.join(ROOT, "profiles"),
-                                       extra_kind=a.only if a.only in ("window", "prefix") else None),
+                                       extra_kind=a.only if a.only in ("window", "prefix", "bwd") else None),
                          indent=1))
         return
     if a.gpus != 1:
@@ -341,6 +419,9 @@ def main():
         return
     if a.only == "prefix":
         prefix_bench(a)
+        return
+    if a.only == "bwd":
+        bwd_bench(a)
         return
 
     import torch

@@ -152,8 +152,8 @@ extern "C" {
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int S, int d_h, float rope_base) {
   if (!bwd_sizes_ok(B, Hq, Hkv, T, S, d_h) || bad_base(rope_base)) return 0;
   const size_t rows = (size_t)B * Hq * T;
-  size_t n = 2 * align256(rows * sizeof(float));
-  if (rope_base > 0.f) n += align256(rows * d_h * 2) + align256((size_t)B * Hkv * S * d_h * 2);
+  size_t n = align256(rows * 16) + align256(rows * d_h * 2);
+  if (rope_base > 0.f) n += align256((size_t)B * Hkv * S * d_h * 2);
   return n;
 }
 
@@ -186,16 +186,12 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
   p.dv = dv;
   const size_t rows = (size_t)B * Hq * T;
   char* ws = (char*)workspace;
-  p.lse2 = (float*)ws;
-  ws += align256(rows * sizeof(float));
-  p.delta = (float*)ws;
-  ws += align256(rows * sizeof(float));
+  p.rec = ws;
+  ws += align256(rows * 16);
+  p.qr = ws;
+  ws += align256(rows * d_h * 2);
   p.use_rope = rope_base > 0.f;
-  if (p.use_rope) {
-    p.qr = ws;
-    ws += align256(rows * d_h * 2);
-    p.kr = ws;
-  }
+  if (p.use_rope) p.kr = ws;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

@@ -96,6 +96,24 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&t0)[kDB], int (&t1)[k
   }
 }
 
+// x as three bf16 pieces hi + mid + lo (each the rounding of what is left), packed as
+// {hi, mid} and {lo, 0}: a matrix product against 1.0 in three k-slots adds x back with
+// fp32 accuracy.  -inf gives {-inf, 0, 0}.
+__device__ __forceinline__ u32x2 split3(float x) {
+  u32x2 r;
+  if (x == -INFINITY) {
+    r[0] = pack_bf16(x, 0.f);
+    r[1] = 0u;
+    return r;
+  }
+  const float hi = bf16_lo(pack_bf16(x, 0.f));
+  const float mid = bf16_lo(pack_bf16(x - hi, 0.f));
+  const float lo = (x - hi) - mid;
+  r[0] = pack_bf16(hi, mid);
+  r[1] = pack_bf16(lo, 0.f);
+  return r;
+}
+
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
 // Rotate pair (x0, x1) back by the RoPE angle of `turns` (the transpose of the rotation).
@@ -110,29 +128,34 @@ __device__ __forceinline__ void unrotate(float& x0, float& x1, float turns) {
 }  // namespace
 
 // ---------------------------------------------------------------- preprocess ----
-// Rows [0, nq) are query rows (b, h, t): delta, lse2 and (RoPE) the rotated q.  Rows
-// [nq, nq + nk) are key rows (b, kvh, s) to rotate (RoPE only).  16 lanes per row, 8
-// elements (4 pairs) per lane.
+// Rows [0, nq) are query rows (b, h, t): the row record (-lse in base 2 and
+// -rowsum(dO * O), each split into bf16 pieces) and q rotated (RoPE) and scaled by
+// log2(e) / sqrt(d_h), so that q_s k'^T are base-2 logits.  Rows [nq, nq + nk) are key rows
+// (b, kvh, s) to rotate (RoPE only).  16 lanes per row, 8 elements (4 pairs) per lane.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long nq, long long nk) {
   const int sub = threadIdx.x % 16;
   const long long nrows = nq + nk;
   const long long stride = (long long)gridDim.x * 16;
+  const float cq = kLog2e / sqrtf((float)kD);
   for (long long row = ((long long)blockIdx.x * 256 + threadIdx.x) / 16; row < nrows; row += stride) {
     if (row < nq) {
       const size_t e0 = (size_t)row * kD + sub * 8;
-      if (p.use_rope) {
-        const int64_t ps = p.pos + (int64_t)(row % p.T);
-        const u32x4 raw = *(const u32x4*)((const __bf16*)p.q + e0);
-        u32x4 outv;
+      const int64_t ps = p.pos + (int64_t)(row % p.T);
+      const u32x4 raw = *(const u32x4*)((const __bf16*)p.q + e0);
+      u32x4 outv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 4; ++e) {
+        float x0 = bf16_lo(raw[e]), x1 = bf16_hi(raw[e]);
+        if (p.use_rope) {
           float sn, cs;
           sincos_rev(rope_turns(ps, p.rope_c[sub * 4 + e]), &sn, &cs);
-          const float x0 = bf16_lo(raw[e]), x1 = bf16_hi(raw[e]);
-          outv[e] = pack_bf16(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+          const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+          x0 = y0;
+          x1 = y1;
         }
-        *(u32x4*)((__bf16*)p.qr + e0) = outv;
+        outv[e] = pack_bf16(x0 * cq, x1 * cq);
       }
+      *(u32x4*)((__bf16*)p.qr + e0) = outv;
       const u32x4 d = *(const u32x4*)((const __bf16*)p.dout + e0);
       const u32x4 o = *(const u32x4*)((const __bf16*)p.out + e0);
       float acc = 0.f;
@@ -143,9 +166,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long nq
       acc += __shfl_xor(acc, 2);
       acc += __shfl_xor(acc, 1);
       if (sub == 0) {
-        p.delta[row] = acc;
         const float l = p.lse[row];
-        p.lse2[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+        const u32x2 nl = split3(l == -INFINITY ? -INFINITY : -l * kLog2e);
+        const u32x2 nd = split3(-acc);
+        *(u32x4*)((char*)p.rec + (size_t)row * 16) = (u32x4){nl[0], nl[1], nd[0], nd[1]};
       }
     } else {
       const long long kr = row - nq;
@@ -167,10 +191,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long nq
 
 // ---------------------------------------------------------------------- dK/dV ----
 __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) u32x4 Qs[2][kTileChunks];  // q' tile, swizzled
+  __shared__ __attribute__((aligned(16))) u32x4 Qs[2][kTileChunks];  // q_s tile, swizzled
   __shared__ __attribute__((aligned(16))) u32x4 Os[2][kTileChunks];  // dO tile, swizzled
-  __shared__ __attribute__((aligned(16))) float Ls[2][kTileRows];    // lse2 of the tile rows
-  __shared__ __attribute__((aligned(16))) float Ds[2][kTileRows];    // delta of the tile rows
+  __shared__ __attribute__((aligned(16))) u32x4 Rs[2][kTileRows];    // row records of the tile
 
   const int tid = threadIdx.x;
   const int wid = tid / kWave;
@@ -204,7 +227,7 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
   const size_t kvrow0 = ((size_t)b * p.Hkv + kvh) * (size_t)S;
   const __bf16* kg = (const __bf16*)(p.use_rope ? p.kr : p.k) + kvrow0 * kD;
   const __bf16* vg = (const __bf16*)p.v + kvrow0 * kD;
-  const __bf16* qbase = (const __bf16*)(p.use_rope ? p.qr : p.q);
+  const __bf16* qbase = (const __bf16*)p.qr;
   const __bf16* obase = (const __bf16*)p.dout;
 
   // k'^T and V^T as B operands: lane holds key `key`, dims ks*16 + g*8 .. +7.
@@ -254,8 +277,7 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
     for (int j = 0; j < 4; ++j) buffer_load_lds16(rq, goff[j], &Qs[BUF][(wid * 4 + j) * kWave]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) buffer_load_lds16(ro, goff[j], &Os[BUF][(wid * 4 + j) * kWave]);
-    if (wid == 0) buffer_load_lds4(make_rsrc(p.lse2 + rowbase, nrows * 4), lane * 4, &Ls[BUF][0]);
-    if (wid == 1) buffer_load_lds4(make_rsrc(p.delta + rowbase, nrows * 4), lane * 4, &Ds[BUF][0]);
+    if (wid == 0) buffer_load_lds16(make_rsrc((const char*)p.rec + rowbase * 16, nrows * 16), lane * 16, &Rs[BUF][0]);
   };
 
   int noff[kKS];  // row reads: row l32, chunk ks*2 + g
@@ -270,73 +292,127 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
     dv[db] = zero16();
     dk[db] = zero16();
   }
-  const float c2 = kLog2e / sqrtf((float)kD);
+  // 1.0 in k-slots 0-2 of the extra k-step that adds a row record's pieces (lanes g = 0)
+  const bf16x8 ones3 = __builtin_bit_cast(bf16x8, (u32x4){g == 0 ? 0x3f803f80u : 0u, g == 0 ? 0x3f80u : 0u, 0u, 0u});
 
-  auto compute = [&](int it, auto bc) {
+  // One 64-query tile against this wave's 32 keys, in four phases that keep the matrix
+  // cores busy while the vector unit works (one wave per SIMD, so the overlap has to come
+  // from the instruction order within the wave):
+  //   A: S0 = q'0 k'^T, dP0 = dO0 V^T (sub-tile 0, queries 0-31)
+  //   B: S1, dP1 for sub-tile 1, with P0 = exp2(S0 c - lse2) and dS0 woven in
+  //   C: dV^T += dO0^T P0, dk'^T += q'0^T dS0, with P1, dS1 woven in
+  //   D: dV^T += dO1^T P1, dk'^T += q'1^T dS1
+  // Each phase's LDS operands are read one phase ahead.  A scheduling barrier after each
+  // pair of products keeps the interleave.  MASK tiles straddle the causal diagonal or the
+  // window edge: there hidden probabilities are set to 0 (32-bit offsets from the key).
+  auto compute = [&](int it, auto bc, auto mc) {
     constexpr int BUF = decltype(bc)::value;
-    const int qb = qb_lo + it % nqb;
+    constexpr bool MASK = decltype(mc)::value;
+    const int q0 = (qb_lo + it % nqb) * kTileRows;
     const char* qt = (const char*)&Qs[BUF][0];
     const char* ot = (const char*)&Os[BUF][0];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int i0 = qb * kTileRows + mi * 32;  // first query of this 32 x 32 tile
-      bool vis = i0 < T && kw0 < S;
-      if (p.causal) vis = vis && (int64_t)kw0 <= pos + i0 + 31;
-      if (p.window > 0) vis = vis && (int64_t)(kw0 + 31) > pos + i0 - p.window;
-      if (!vis) continue;
-      f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const bf16x8 aq = *(const bf16x8*)(qt + noff[ks] + mi * 32 * kRowBytes);
-        const bf16x8 ao = *(const bf16x8*)(ot + noff[ks] + mi * 32 * kRowBytes);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kop[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vop[ks], dp, 0, 0, 0);
-      }
-      // statistics of this lane's 16 rows: rows mi*32 + q*8 + g*4 + (0..3)
-      f32x4 lr[4], dr[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        lr[q] = *(const f32x4*)&Ls[BUF][mi * 32 + q * 8 + g * 4];
-        dr[q] = *(const f32x4*)&Ds[BUF][mi * 32 + q * 8 + g * 4];
-      }
-      float pr[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(s[r], c2, -lr[r / 4][r % 4]));
-      const bool need_mask = (p.causal && (int64_t)(kw0 + 31) > pos + i0) ||
-                             (p.window > 0 && (int64_t)kw0 <= pos + i0 + 31 - p.window);
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t lim = pos + i0 + (r / 4) * 8 + g * 4 + (r % 4);  // last key this row sees
-          const bool ok = (int64_t)key <= lim && (p.window <= 0 || (int64_t)key > lim - p.window);
-          if (!ok) pr[r] = 0.f;
-        }
-      }
-      bf16x8 pb[2], db2[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4 pk, dk4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * h + 2 * e;
-          pk[e] = pack_bf16(pr[r], pr[r + 1]);
-          dk4[e] = pack_bf16(pr[r] * (dp[r] - dr[r / 4][r % 4]), pr[r + 1] * (dp[r + 1] - dr[r / 4][(r + 1) % 4]));
-        }
-        pb[h] = __builtin_bit_cast(bf16x8, pk);
-        db2[h] = __builtin_bit_cast(bf16x8, dk4);
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rb = (mi * 2 + h) * 16 * kRowBytes;  // rows of this 16-query k-step
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const bf16x8 ao = tr_read(ot + rb + toff0[db], ot + rb + toff1[db]);
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[h], dv[db], 0, 0, 0);
-          const bf16x8 aq = tr_read(qt + rb + toff0[db], qt + rb + toff1[db]);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, db2[h], dk[db], 0, 0, 0);
-        }
-      }
+    // rel(r, mi) = key - (pos + query) = relb - (mi*32 + (r/4)*8 + r%4); visible iff
+    // rel <= 0 and rel > -wlim
+    int relb = 0, wlim = 0x7fffffff;
+    if constexpr (MASK) {
+      int64_t r64 = (int64_t)key - g * 4 - pos - q0;
+      r64 = r64 > (1 << 30) ? (1 << 30) : (r64 < -(1 << 30) ? -(1 << 30) : r64);
+      relb = (int)r64;
+      if (p.window > 0) wlim = (int)(p.window < (1 << 30) ? p.window : (1 << 30));
     }
+    auto rowrd = [&](const char* t, int mi, int ks) {
+      return *(const bf16x8*)(t + noff[ks] + mi * 32 * kRowBytes);
+    };
+    auto trrd = [&](const char* t, int mi, int h, int db) {
+      const int rb = (mi * 2 + h) * 16 * kRowBytes;
+      return tr_read(t + rb + toff0[db], t + rb + toff1[db]);
+    };
+    // p and dS of element r of a sub-tile, in place (s <- p, dp <- dS); the products
+    // already hold s - lse2 and dP - rowsum(dO * O)
+    auto elem = [&](f32x16& s, f32x16& dp, int mi, int r) {
+      float pv = fast_exp2(s[r]);
+      if constexpr (MASK) {
+        const int rel = relb - (mi * 32 + (r / 4) * 8 + (r % 4));
+        pv = (rel <= 0 && rel > -wlim) ? pv : 0.f;
+      }
+      s[r] = pv;
+      dp[r] = pv * dp[r];
+    };
+    // the row records of sub-tile mi as the A operands of the extra k-step
+    auto bias = [&](int mi, bf16x8& bl, bf16x8& bd) {
+      const u32x4 r = Rs[BUF][mi * 32 + l32];
+      const uint32_t m = g == 0 ? 0xffffffffu : 0u;
+      bl = __builtin_bit_cast(bf16x8, (u32x4){r[0] & m, r[1] & m, 0u, 0u});
+      bd = __builtin_bit_cast(bf16x8, (u32x4){r[2] & m, r[3] & m, 0u, 0u});
+    };
+    auto pack = [&](const f32x16& x, int h) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16(x[8 * h + 2 * e], x[8 * h + 2 * e + 1]);
+      return __builtin_bit_cast(bf16x8, w);
+    };
+
+    bf16x8 a0[kKS], b0[kKS], a1[kKS], b1[kKS];
+    bf16x8 to0[2][kDB], tq0[2][kDB], to1[2][kDB], tq1[2][kDB];
+    bf16x8 bl0, bd0, bl1, bd1;
+    bias(0, bl0, bd0);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      a0[ks] = rowrd(qt, 0, ks);
+      b0[ks] = rowrd(ot, 0, ks);
+    }
+    bias(1, bl1, bd1);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- A (reads sub-tile 1's rows as sub-tile 0's are consumed)
+    f32x16 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl0, ones3, zero16(), 0, 0, 0);
+    f32x16 d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bd0, ones3, zero16(), 0, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[ks], kop[ks], s0, 0, 0, 0);
+      d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0[ks], vop[ks], d0, 0, 0, 0);
+      a1[ks] = rowrd(qt, 1, ks);
+      b1[ks] = rowrd(ot, 1, ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- B (reads sub-tile 0's transposed operands)
+    f32x16 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl1, ones3, zero16(), 0, 0, 0);
+    f32x16 d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bd1, ones3, zero16(), 0, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[ks], kop[ks], s1, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1[ks], vop[ks], d1, 0, 0, 0);
+      elem(s0, d0, 0, 2 * ks);
+      elem(s0, d0, 0, 2 * ks + 1);
+      to0[ks / kDB][ks % kDB] = trrd(ot, 0, ks / kDB, ks % kDB);
+      tq0[ks / kDB][ks % kDB] = trrd(qt, 0, ks / kDB, ks % kDB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const bf16x8 pb0[2] = {pack(s0, 0), pack(s0, 1)};
+    const bf16x8 ds0[2] = {pack(d0, 0), pack(d0, 1)};
+    // ---- C (reads sub-tile 1's transposed operands)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to0[h][db], pb0[h], dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq0[h][db], ds0[h], dk[db], 0, 0, 0);
+        elem(s1, d1, 1, 2 * (h * kDB + db));
+        elem(s1, d1, 1, 2 * (h * kDB + db) + 1);
+        to1[h][db] = trrd(ot, 1, h, db);
+        tq1[h][db] = trrd(qt, 1, h, db);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    const bf16x8 pb1[2] = {pack(s1, 0), pack(s1, 1)};
+    const bf16x8 ds1[2] = {pack(d1, 0), pack(d1, 1)};
+    // ---- D
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to1[h][db], pb1[h], dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq1[h][db], ds1[h], dk[db], 0, 0, 0);
+      }
   };
 
   // Tile it lives in buffer it & 1 (a compile-time constant in each step, so the compiler
@@ -345,7 +421,21 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
     constexpr int BUF = decltype(bc)::value;
     __syncthreads();  // tile it has landed; everyone is done with tile it-1
     if (it + 1 < n_it) load_tile(it + 1, std::integral_constant<int, BUF ^ 1>{});
-    compute(it, bc);
+    // which of this wave's (query, key) pairs in the tile are visible
+    const int64_t q0 = (int64_t)(qb_lo + it % nqb) * kTileRows;
+    bool any = kw0 < S, all = true;
+    if (p.causal) {
+      any = any && (int64_t)kw0 <= pos + q0 + kTileRows - 1;
+      all = (int64_t)(kw0 + 31) <= pos + q0;
+    }
+    if (p.window > 0) {
+      any = any && (int64_t)(kw0 + 31) > pos + q0 - p.window;
+      all = all && (int64_t)kw0 > pos + q0 + kTileRows - 1 - p.window;
+    }
+    if (any) {
+      if (all) compute(it, bc, std::false_type{});
+      else compute(it, bc, std::true_type{});
+    }
     wait_loads();
   };
   if (n_it > 0) {
@@ -357,11 +447,12 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
     if (it + 1 < n_it) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
-  // ---- epilogue: dV, and dk = R^T dk' with dk' = dk'^T / sqrt(d_h) (pairs are in-lane).
+  // ---- epilogue: dV, and dk = R^T dk' with dk' = dS^T q' / sqrt(d_h) = ln(2) dS^T q_s
+  // (pairs are in-lane).
   if (key < S) {
     __bf16* dvg = (__bf16*)p.dv + (kvrow0 + key) * kD;
     __bf16* dkg = (__bf16*)p.dk + (kvrow0 + key) * kD;
-    const float isd = 1.f / sqrtf((float)kD);
+    const float isd = kLn2;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
@@ -423,15 +514,14 @@ void bwd_dq_kernel(BwdParams p) {
   const int t = wrow0 + l32;                            // this lane's query
 
   const size_t row = ((size_t)b * p.Hq + hq) * (size_t)T + t;
-  const __bf16* qg = (const __bf16*)(p.use_rope ? p.qr : p.q);
+  const __bf16* qg = (const __bf16*)p.qr;
   const __bf16* og = (const __bf16*)p.dout;
   const size_t kvrow0 = ((size_t)b * p.Hkv + kvh) * (size_t)S;
   const __bf16* kg = (const __bf16*)(p.use_rope ? p.kr : p.k) + kvrow0 * kD;
   const __bf16* vg = (const __bf16*)p.v + kvrow0 * kD;
 
-  // q'^T and dO^T as B operands: lane holds query t, dims ks*16 + g*8 .. +7.
+  // q_s^T and dO^T as B operands: lane holds query t, dims ks*16 + g*8 .. +7.
   bf16x8 qop[kKS], dop[kKS];
-  float lse2 = INFINITY, delta = 0.f;  // rows past T: probabilities 0
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) {
     u32x4 qr = {0u, 0u, 0u, 0u}, orw = {0u, 0u, 0u, 0u};
@@ -442,10 +532,17 @@ void bwd_dq_kernel(BwdParams p) {
     qop[ks] = __builtin_bit_cast(bf16x8, qr);
     dop[ks] = __builtin_bit_cast(bf16x8, orw);
   }
-  if (t < T) {
-    lse2 = p.lse2[row];
-    delta = p.delta[row];
+  // The row record as the B operands of the extra k-step (rows past T: -inf, so their
+  // probabilities are 0); the K / V side holds 1.0 in the matching k-slots.
+  bf16x8 bl, bd;
+  {
+    u32x4 r = {0xff80u, 0u, 0u, 0u};
+    if (t < T) r = *(const u32x4*)((const char*)p.rec + row * 16);
+    const uint32_t m = g == 0 ? 0xffffffffu : 0u;
+    bl = __builtin_bit_cast(bf16x8, (u32x4){r[0] & m, r[1] & m, 0u, 0u});
+    bd = __builtin_bit_cast(bf16x8, (u32x4){r[2] & m, r[3] & m, 0u, 0u});
   }
+  const bf16x8 ones3 = __builtin_bit_cast(bf16x8, (u32x4){g == 0 ? 0x3f803f80u : 0u, g == 0 ? 0x3f80u : 0u, 0u, 0u});
 
   // ---- keys visible to this wave / to the workgroup (as in the forward kernel).
   int nk_wave = S, nk_wg = S;
@@ -494,7 +591,6 @@ void bwd_dq_kernel(BwdParams p) {
   f32x16 dq[kDB];
 #pragma unroll
   for (int db = 0; db < kDB; ++db) dq[db] = zero16();
-  const float c2 = kLog2e / sqrtf((float)kD);
 
   auto compute = [&](int tile, auto bc) {
     constexpr int BUF = decltype(bc)::value;
@@ -508,7 +604,8 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       bf16x8 dsb[2];
-      f32x16 s = zero16(), dp = zero16();
+      f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones3, bl, zero16(), 0, 0, 0);
+      f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones3, bd, zero16(), 0, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
         const bf16x8 ak = *(const bf16x8*)(kt + noff[ks] + mb * 32 * kRowBytes);
@@ -518,7 +615,7 @@ void bwd_dq_kernel(BwdParams p) {
       }
       float pr[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(s[r], c2, -lse2));
+      for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(s[r]);
       if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -533,7 +630,7 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 8 * h + 2 * e;
-          pk[e] = pack_bf16(pr[r] * (dp[r] - delta), pr[r + 1] * (dp[r + 1] - delta));
+          pk[e] = pack_bf16(pr[r] * dp[r], pr[r + 1] * dp[r + 1]);
         }
         dsb[h] = __builtin_bit_cast(bf16x8, pk);
       }

@@ -45,9 +45,9 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* lse2;      // [B, Hq, T] lse * log2(e); +inf for rows with no visible key
-  float* delta;     // [B, Hq, T] rowsum(dout * out)
-  void* qr;         // [B, Hq, T, d_h] bf16 rotated q (RoPE), else null
+  void* rec;        // [B, Hq, T] 16-byte row records: -lse*log2(e) and -rowsum(dout * out),
+                    // each as three bf16 pieces (hi, mid, lo) and a zero
+  void* qr;         // [B, Hq, T, d_h] bf16 q, rotated (RoPE) and scaled by log2(e) / sqrt(d_h)
   void* kr;         // [B, Hkv, S, d_h] bf16 rotated k (RoPE), else null
   int B, Hq, Hkv, T, S;
   int causal;

@@ -147,13 +147,13 @@ def test_bwd_validation(lib, kw, status):
 
 def test_bwd_workspace_bytes(lib):
     import exact_transformer_attention_amd as e
-    # two fp32 per query row (lse in base 2, rowsum(dO * O)), each array 256-byte aligned;
-    # with RoPE also the rotated q and k in bf16
+    # a 16-byte record per query row and the scaled (rotated) q in bf16, each array 256-byte
+    # aligned; with RoPE also the rotated k in bf16
     rows = 2 * 32 * 8192
-    assert e.attn_bwd_workspace_bytes(2, 32, 8, 8192, 8192, 128, 0.0) == 2 * rows * 4
-    assert e.attn_bwd_workspace_bytes(2, 32, 8, 8192, 8192, 128, 1e4) == 2 * rows * 4 + rows * 256 + 2 * 8 * 8192 * 256
-    assert e.attn_bwd_workspace_bytes(1, 1, 1, 3, 5, 128, 0.0) == 2 * 256
-    assert e.attn_bwd_workspace_bytes(1, 1, 1, 3, 5, 128, 1e4) == 2 * 256 + 768 + 1280
+    assert e.attn_bwd_workspace_bytes(2, 32, 8, 8192, 8192, 128, 0.0) == rows * 16 + rows * 256
+    assert e.attn_bwd_workspace_bytes(2, 32, 8, 8192, 8192, 128, 1e4) == rows * 16 + rows * 256 + 2 * 8 * 8192 * 256
+    assert e.attn_bwd_workspace_bytes(1, 1, 1, 3, 5, 128, 0.0) == 256 + 768
+    assert e.attn_bwd_workspace_bytes(1, 1, 1, 3, 5, 128, 1e4) == 256 + 768 + 1280
     assert e.attn_bwd_workspace_bytes(1, 6, 4, 3, 5, 128, 0.0) == 0
     assert e.attn_bwd_workspace_bytes(1, 1, 1, 3, 5, 128, -1.0) == 0
 
