@@ -191,9 +191,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long nq
 
 // ---------------------------------------------------------------------- dK/dV ----
 __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) u32x4 Qs[2][kTileChunks];  // q_s tile, swizzled
-  __shared__ __attribute__((aligned(16))) u32x4 Os[2][kTileChunks];  // dO tile, swizzled
-  __shared__ __attribute__((aligned(16))) u32x4 Rs[2][kTileRows];    // row records of the tile
+  // Double-buffered q_s and dO tiles (swizzled) and row records; one array per buffer (see
+  // the dQ kernel).
+  __shared__ __attribute__((aligned(16))) u32x4 Qs0[kTileChunks], Qs1[kTileChunks];
+  __shared__ __attribute__((aligned(16))) u32x4 Os0[kTileChunks], Os1[kTileChunks];
+  __shared__ __attribute__((aligned(16))) u32x4 Rs0[kTileRows], Rs1[kTileRows];
 
   const int tid = threadIdx.x;
   const int wid = tid / kWave;
@@ -273,11 +275,13 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
     const uint32_t nrows = (uint32_t)min(T - q0, kTileRows);
     const i32x4 rq = make_rsrc(qbase + rowbase * kD, nrows * kRowBytes);
     const i32x4 ro = make_rsrc(obase + rowbase * kD, nrows * kRowBytes);
+    u32x4* qd = BUF ? Qs1 : Qs0;
+    u32x4* od = BUF ? Os1 : Os0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) buffer_load_lds16(rq, goff[j], &Qs[BUF][(wid * 4 + j) * kWave]);
+    for (int j = 0; j < 4; ++j) buffer_load_lds16(rq, goff[j], qd + (wid * 4 + j) * kWave);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) buffer_load_lds16(ro, goff[j], &Os[BUF][(wid * 4 + j) * kWave]);
-    if (wid == 0) buffer_load_lds16(make_rsrc((const char*)p.rec + rowbase * 16, nrows * 16), lane * 16, &Rs[BUF][0]);
+    for (int j = 0; j < 4; ++j) buffer_load_lds16(ro, goff[j], od + (wid * 4 + j) * kWave);
+    if (wid == 0) buffer_load_lds16(make_rsrc((const char*)p.rec + rowbase * 16, nrows * 16), lane * 16, BUF ? Rs1 : Rs0);
   };
 
   int noff[kKS];  // row reads: row l32, chunk ks*2 + g
@@ -309,8 +313,9 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
     constexpr int BUF = decltype(bc)::value;
     constexpr bool MASK = decltype(mc)::value;
     const int q0 = (qb_lo + it % nqb) * kTileRows;
-    const char* qt = (const char*)&Qs[BUF][0];
-    const char* ot = (const char*)&Os[BUF][0];
+    const char* qt = (const char*)(BUF ? Qs1 : Qs0);
+    const char* ot = (const char*)(BUF ? Os1 : Os0);
+    const u32x4* rt = BUF ? Rs1 : Rs0;
     // rel(r, mi) = key - (pos + query) = relb - (mi*32 + (r/4)*8 + r%4); visible iff
     // rel <= 0 and rel > -wlim
     int relb = 0, wlim = 0x7fffffff;
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
     };
     // the row records of sub-tile mi as the A operands of the extra k-step
     auto bias = [&](int mi, bf16x8& bl, bf16x8& bd) {
-      const u32x4 r = Rs[BUF][mi * 32 + l32];
+      const u32x4 r = rt[mi * 32 + l32];
       const uint32_t m = g == 0 ? 0xffffffffu : 0u;
       bl = __builtin_bit_cast(bf16x8, (u32x4){r[0] & m, r[1] & m, 0u, 0u});
       bd = __builtin_bit_cast(bf16x8, (u32x4){r[2] & m, r[3] & m, 0u, 0u});
@@ -480,8 +485,11 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
 template <int HP>
 __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(kQW / 4, kQW / 4)))
 void bwd_dq_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) u32x4 Ks[2][kTileChunks];  // k' tile, swizzled
-  __shared__ __attribute__((aligned(16))) u32x4 Vs[2][kTileChunks];  // V tile, swizzled
+  // Double-buffered k' and V tiles (swizzled).  Each buffer is its own array so that the
+  // compiler can tell the tile being read from the one whose direct-to-LDS loads are in
+  // flight (it does not separate two halves of one array) and need not wait for them.
+  __shared__ __attribute__((aligned(16))) u32x4 Ks0[kTileChunks], Ks1[kTileChunks];
+  __shared__ __attribute__((aligned(16))) u32x4 Vs0[kTileChunks], Vs1[kTileChunks];
 
   const int tid = threadIdx.x;
   const int wid = tid / kWave;
@@ -576,10 +584,12 @@ void bwd_dq_kernel(BwdParams p) {
     const uint32_t nrows = (uint32_t)min(S - k0, kTileRows);
     const i32x4 rk = make_rsrc(kg + (size_t)k0 * kD, nrows * kRowBytes);
     const i32x4 rv = make_rsrc(vg + (size_t)k0 * kD, nrows * kRowBytes);
+    u32x4* kd = BUF ? Ks1 : Ks0;
+    u32x4* vd = BUF ? Vs1 : Vs0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) buffer_load_lds16(rk, goff[j], &Ks[BUF][(wid * 2 + j) * kWave]);
+    for (int j = 0; j < 2; ++j) buffer_load_lds16(rk, goff[j], kd + (wid * 2 + j) * kWave);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) buffer_load_lds16(rv, goff[j], &Vs[BUF][(wid * 2 + j) * kWave]);
+    for (int j = 0; j < 2; ++j) buffer_load_lds16(rv, goff[j], vd + (wid * 2 + j) * kWave);
   };
 
   int noff[kKS];
@@ -596,8 +606,8 @@ void bwd_dq_kernel(BwdParams p) {
     constexpr int BUF = decltype(bc)::value;
     const int k0 = tile * kTileRows;
     if (!(k0 < nk_wave && (int64_t)(k0 + kTileRows) > lo_wave)) return;
-    const char* kt = (const char*)&Ks[BUF][0];
-    const char* vt = (const char*)&Vs[BUF][0];
+    const char* kt = (const char*)(BUF ? Ks1 : Ks0);
+    const char* vt = (const char*)(BUF ? Vs1 : Vs0);
     const bool need_mask = (k0 + kTileRows > S) || (p.causal && (int64_t)(k0 + kTileRows - 1) > pos + wrow0) ||
                            (p.window > 0 && (int64_t)k0 < lo_wave + 31);
     const int64_t lim = pos + t;  // last key this lane's query sees
