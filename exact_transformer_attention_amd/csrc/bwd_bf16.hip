@@ -257,6 +257,10 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
   const int qb_lo = (int)(qlo / kTileRows);
   const int nqb = qhi > qlo ? (int)((qhi + kTileRows - 1) / kTileRows) - qb_lo : 0;
   const int n_it = G * nqb;
+  // Iteration it reads query tile qb_top - it / G of head it % G: every workgroup walks the
+  // tiles from the top down with the heads innermost, so the workgroups of one KV head
+  // that run together read the same tile at about the same time (shared in L2).
+  const int qb_top = qb_lo + nqb - 1;
 
   // ---- tile loads: this thread's chunks of rows row0 + 4j (direct to LDS, swizzled).
   const int slot = lane % kCPR;
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
   }
   auto load_tile = [&](int it, auto bc) {
     constexpr int BUF = decltype(bc)::value;
-    const int hh = it / nqb, qb = qb_lo + it % nqb;
+    const int hh = it % G, qb = qb_top - it / G;
     const int q0 = qb * kTileRows;
     const size_t rowbase = ((size_t)b * p.Hq + (size_t)kvh * G + hh) * (size_t)T + q0;
     const uint32_t nrows = (uint32_t)min(T - q0, kTileRows);
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
   auto compute = [&](int it, auto bc, auto mc) {
     constexpr int BUF = decltype(bc)::value;
     constexpr bool MASK = decltype(mc)::value;
-    const int q0 = (qb_lo + it % nqb) * kTileRows;
+    const int q0 = (qb_top - it / G) * kTileRows;
     const char* qt = (const char*)(BUF ? Qs1 : Qs0);
     const char* ot = (const char*)(BUF ? Os1 : Os0);
     const u32x4* rt = BUF ? Rs1 : Rs0;
@@ -427,7 +431,7 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
     __syncthreads();  // tile it has landed; everyone is done with tile it-1
     if (it + 1 < n_it) load_tile(it + 1, std::integral_constant<int, BUF ^ 1>{});
     // which of this wave's (query, key) pairs in the tile are visible
-    const int64_t q0 = (int64_t)(qb_lo + it % nqb) * kTileRows;
+    const int64_t q0 = (int64_t)(qb_top - it / G) * kTileRows;
     bool any = kw0 < S, all = true;
     if (p.causal) {
       any = any && (int64_t)kw0 <= pos + q0 + kTileRows - 1;
