@@ -217,6 +217,6 @@ def scaled(cfg, **overrides):
     return c
 
 
-__all__ = ["CONFIGS", "make_fwd_inputs", "make_decode_inputs", "make_prefill_paged_inputs", "fwd_flops",
-           "window_flops", "prefill_paged_flops", "decode_kv_bytes",
+__all__ = ["CONFIGS", "make_fwd_inputs", "make_bwd_inputs", "make_decode_inputs", "make_prefill_paged_inputs",
+           "fwd_flops", "bwd_flops", "window_flops", "prefill_paged_flops", "decode_kv_bytes",
            "fwd_io_bytes", "scaled", "torch_dtype"]
