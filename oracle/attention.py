@@ -398,6 +398,34 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, block_size, rope_ba
     return out, lse
 
 
+# ---------------------------------------------------------------- fp8 ----
+
+def fp8_e4m3_decode(codes):
+    """Values of 8-bit floating-point codes in the E4M3 format of the OCP 8-bit floating point
+    specification (the fp8 operand format of gfx950's matrix cores): sign bit, 4-bit exponent
+    with bias 7, 3-bit mantissa; exponent 0 encodes subnormals (m/8)*2^-6; S.1111.111 is NaN
+    and there is no infinity, so the largest finite magnitude is 1.75*2^8 = 448.  The pages
+    name FP8 only as a feature of newer hardware ("Why is attention O(n^2) ...", later
+    FlashAttention versions); the format is this reading."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(F64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.power(2.0, (e - 7).astype(F64)))
+    mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def attention_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, causal=False, pos=0):
+    """Exact attention on fp8 inputs, the values being code * scale per tensor: q8 [B,Hq,T,d_h],
+    k8 [B,Hkv,S,d_h] and V given transposed, vt8 [B,Hkv,d_h,S] (uint8 codes).  q and k are
+    taken as already rotated (no RoPE).  Returns attention(q, k, v, causal, pos=pos) in fp64."""
+    q = fp8_e4m3_decode(q8) * F64(q_scale)
+    k = fp8_e4m3_decode(k8) * F64(k_scale)
+    v = np.swapaxes(fp8_e4m3_decode(vt8), -1, -2) * F64(v_scale)
+    return attention(q, k, v, causal=causal, pos=pos)
+
+
 # ------------------------------------------------------------ metrics ----
 
 def max_abs(got, ref):

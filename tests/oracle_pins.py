@@ -657,7 +657,50 @@ def check_backward_sampled_equals_full(orc):
         assert np.allclose(b_, dk[1, 1, keys], atol=1e-13) and np.allclose(c, dv[1, 1, keys], atol=1e-13)
 
 
+# ------------------------------------------------------------------------
+# FP8 inputs
+# ------------------------------------------------------------------------
+
+def check_fp8_decode(orc):
+    """The E4M3 decoder against the format's closed forms (1.0, the largest finite 448, the
+    smallest normal 2^-6 and subnormal 2^-9, signs, NaN), monotone over the positive codes, and
+    against torch's float8_e4m3fn conversion for all 256 codes (a library cross-check)."""
+    d = orc.fp8_e4m3_decode
+    assert d(0x38) == 1.0 and d(0xB8) == -1.0 and d(0x7E) == 448.0 and d(0xFE) == -448.0
+    assert d(0x08) == 2.0 ** -6 and d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9 and d(0x00) == 0.0
+    assert d(0x3C) == 1.5 and d(0x40) == 2.0 and d(0x30) == 0.5
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+    pos = d(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = d(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(got)) and np.array_equal(ref[~np.isnan(ref)], got[~np.isnan(got)])
+
+
+def check_fp8_attention_scales(orc):
+    """Per-tensor scales: multiplying q's scale by a and dividing k's by a leaves the logits
+    and so the output unchanged; v's scale multiplies the output and leaves lse unchanged; V is
+    read transposed ([.., d_h, S]), which a per-element loop over the decoded codes checks."""
+    rng = _rng(40)
+    q8 = rng.integers(0, 0x70, (1, 4, 9, 16)).astype(np.uint8) | (rng.integers(0, 2, (1, 4, 9, 16)) << 7).astype(np.uint8)
+    k8 = rng.integers(0, 0x70, (1, 2, 11, 16)).astype(np.uint8)
+    vt8 = rng.integers(0, 0x70, (1, 2, 16, 11)).astype(np.uint8) | 0x80
+    o1, l1 = orc.attention_fp8(q8, k8, vt8, 1.0, 1.0, 1.0, causal=True, pos=2)
+    o2, l2 = orc.attention_fp8(q8, k8, vt8, 4.0, 0.25, 3.0, causal=True, pos=2)
+    assert np.allclose(o2, 3.0 * o1, atol=1e-12) and np.allclose(l2, l1, atol=1e-12)
+    d = orc.fp8_e4m3_decode
+    v = np.zeros((1, 2, 11, 16))
+    for h in range(2):
+        for sk in range(11):
+            for e in range(16):
+                v[0, h, sk, e] = d(vt8[0, h, e, sk])
+    ro, rl = brute_force_attention(d(q8), d(k8), v, True, 0.0, 2)
+    assert np.allclose(o1, ro, atol=1e-12) and np.allclose(l1, rl, atol=1e-12)
+
+
 ALL_CHECKS = [
+    check_fp8_decode, check_fp8_attention_scales,
     check_backward_finite_differences, check_backward_sampled_equals_full, check_backward_torch_autograd, check_backward_invariants,
     check_prefill_paged_equals_contiguous,
     check_bruteforce_window,

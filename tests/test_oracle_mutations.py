@@ -233,7 +233,23 @@ def m_bwd_dk_uses_unrotated_q(mod):
               "dk[b, g] += apply_rope_transpose(ds.T @ q[b, h] * scale, kpos, rope_base)")
 
 
-MUTATIONS = [m_bwd_missing_delta, m_bwd_rope_forward_not_transpose, m_bwd_gqa_overwrite,
+def m_fp8_bias8(mod):
+    """E4M3 exponent bias 8 instead of 7."""
+    _resource(mod, "np.power(2.0, (e - 7).astype(F64))", "np.power(2.0, (e - 8).astype(F64))")
+
+
+def m_fp8_no_subnormals(mod):
+    """Exponent 0 decoded as a normal number."""
+    _resource(mod, "mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6,", "mag = np.where(e < 0, (m / 8.0) * 2.0 ** -6,")
+
+
+def m_fp8_v_not_transposed(mod):
+    """V codes read as [.., S, d_h] instead of transposed."""
+    _resource(mod, "v = np.swapaxes(fp8_e4m3_decode(vt8), -1, -2) * F64(v_scale)",
+              "v = fp8_e4m3_decode(vt8).reshape(vt8.shape[:-2] + (vt8.shape[-1], vt8.shape[-2])) * F64(v_scale)")
+
+
+MUTATIONS = [m_fp8_bias8, m_fp8_no_subnormals, m_fp8_v_not_transposed, m_bwd_missing_delta, m_bwd_rope_forward_not_transpose, m_bwd_gqa_overwrite,
              m_bwd_dk_unscaled, m_bwd_dk_uses_unrotated_q,
              m_window_off_by_one, m_mask_after_softmax, m_no_scale, m_scale_by_d, m_rope_freq_exponent, m_rope_clockwise,
              m_rope_rotate_half_pairs, m_rope_only_queries, m_gqa_modulo, m_causal_off_by_one,
