@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libattn.so")
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
 ATTN_F32, ATTN_BF16 = 0, 1
 
-EXPORTED = ("attn_fwd", "attn_fwd_window", "attn_prefill_paged", "attn_decode_paged",
+EXPORTED = ("attn_fwd", "attn_fwd_window", "attn_fwd_fp8", "attn_prefill_paged", "attn_decode_paged",
             "attn_decode_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes", "attn_paged_gather",
             "attn_status_str")
 
@@ -40,6 +40,8 @@ def _load():
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_paged_gather.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.attn_paged_gather.restype = i32
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i64, vp]
+    lib.attn_fwd_fp8.restype = i32
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, f32,
                              i64, vp, sz, i32, vp]
     lib.attn_bwd.restype = i32
@@ -130,6 +132,30 @@ def attn_fwd_window(q, k, v, window, rope_base=0.0, pos=0, out=None, lse=None, w
     st = LIB.attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, T, S, d,
                              int(window), float(rope_base), int(pos), _dtype_code(q), _stream(stream))
     _check(st, "attn_fwd_window")
+    return out, lse
+
+
+def attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, causal=False, pos=0, out=None, lse=None, want_lse=True,
+                 stream=None):
+    """Exact attention on fp8 (E4M3) inputs: q8 [B,Hq,T,d_h], k8 [B,Hkv,S,d_h] and V transposed
+    vt8 [B,Hkv,d_h,S], uint8 (or float8_e4m3fn) device tensors of codes, value = code * scale.
+    Returns (out bf16 [B,Hq,T,d_h], lse fp32 [B,Hq,T])."""
+    import torch
+    for t in (q8, k8, vt8):
+        _require(t.dim() == 4 and t.element_size() == 1 and t.is_cuda and t.is_contiguous(),
+                 "q8, k8, vt8 must be contiguous 4-D one-byte device tensors")
+    B, Hq, T, d = q8.shape
+    Hkv, S = k8.shape[1], k8.shape[2]
+    _require(k8.shape == (B, Hkv, S, d) and vt8.shape == (B, Hkv, d, S), "shape mismatch")
+    if out is None:
+        out = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q8.device)
+    _require(out.shape == (B, Hq, T, d) and out.dtype == torch.bfloat16 and out.is_contiguous(), "bad out")
+    st = LIB.attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), _ptr(out), _ptr(lse), B, Hq, Hkv, T, S, d,
+                          int(bool(causal)), float(q_scale), float(k_scale), float(v_scale), int(pos),
+                          _stream(stream))
+    _check(st, "attn_fwd_fp8")
     return out, lse
 
 

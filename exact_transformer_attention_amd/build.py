@@ -17,13 +17,14 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["api.cpp", "fwd_f32.hip", "fwd_bf16.hip", "decode.hip", "bwd_bf16.hip"]
+SOURCES = ["api.cpp", "fwd_f32.hip", "fwd_bf16.hip", "fwd_fp8.hip", "decode.hip", "bwd_bf16.hip"]
 # Per-source extra flags.  The attention kernels keep MFMA accumulators in VGPRs (their
 # softmax reads every accumulator with VALU instructions; AGPR-form accumulators cost a
 # copy per element per block).
 EXTRA_FLAGS = {"fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-               "bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+               "bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+               "fwd_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

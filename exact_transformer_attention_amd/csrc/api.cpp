@@ -95,6 +95,40 @@ attn_status_t attn_fwd_window(const void* q, const void* k, const void* v, void*
   return fwd_impl(q, k, v, out, lse, B, Hq, Hkv, T, S, d_h, 1, window, rope_base, pos, dtype, stream);
 }
 
+attn_status_t attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* out, float* lse, int B, int Hq,
+                           int Hkv, int T, int S, int d_h, int causal, float q_scale, float k_scale, float v_scale,
+                           int64_t pos, void* stream) {
+  if (!q8 || !k8 || !vt8 || !out) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || d_h < 1) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  for (float sc : {q_scale, k_scale, v_scale})
+    if (!(std::isfinite(sc) && sc > 0.f)) return ATTN_ERR_INVALID_ARG;
+  if (d_h != 128 || S % 4 != 0 || ((uintptr_t)vt8 & 3) != 0) return ATTN_ERR_UNSUPPORTED;
+  if (pos > ((int64_t)1 << 40) || pos < -((int64_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
+  if ((size_t)d_h * S > 0xffffffffu) return ATTN_ERR_UNSUPPORTED;
+
+  attn::FwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q8;
+  p.k = k8;
+  p.v = vt8;
+  p.out = out;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.T = T;
+  p.S = S;
+  p.causal = causal;
+  p.pos = pos;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  hipError_t e = attn::launch_fwd_fp8(p, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status_t attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* block_table, const int32_t* seq_lens, int block_size,
                                  int num_seqs, int Hq, int Hkv, int d_h, int T, int max_blocks_per_seq,

@@ -11,6 +11,7 @@ namespace attn {
 
 hipError_t launch_fwd_f32(const FwdParams& p, int d_h, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdParams& p, int d_h, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdParams& p, hipStream_t stream);
 
 // Backward: preprocess, dK/dV and dQ kernels, enqueued in that order.
 hipError_t launch_bwd_bf16(BwdParams p, hipStream_t stream);

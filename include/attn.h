@@ -90,6 +90,26 @@ ATTN_API attn_status_t attn_fwd_window(const void* q, const void* k, const void*
                                        attn_dtype_t dtype, void* stream);
 
 /*
+ * attn_fwd_fp8 -- exact attention with fp8 inputs and fp8 matrix products ("Why is attention
+ * O(n^2), how does FlashAttention help ...", Deep dive: later FlashAttention versions exploit
+ * newer hardware such as FP8), same definition and masking as attn_fwd.
+ *
+ *   q8       [B, Hq, T, d_h]   E4M3 codes (OCP 8-bit float: bias 7, largest 448, no infinity)
+ *   k8       [B, Hkv, S, d_h]  E4M3 codes
+ *   vt8      [B, Hkv, d_h, S]  E4M3 codes of V, transposed (d_h-major), 4-byte aligned
+ *   q_scale, k_scale, v_scale  > 0: the value of a code c of that tensor is c * scale
+ *   out      [B, Hq, T, d_h] bf16;  lse [B, Hq, T] fp32 or NULL (as attn_fwd)
+ *   causal, pos  as attn_fwd.  q and k are used as given (already rotated: no RoPE).
+ * Both products run on E4M3 matrix cores with fp32 accumulation; the probabilities are
+ * rounded to E4M3 for the P V product, the softmax normaliser uses them unrounded.
+ * Supported: d_h == 128, S % 4 == 0 (ATTN_ERR_UNSUPPORTED otherwise); codes must not be NaN.
+ */
+ATTN_API attn_status_t attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* out,
+                                    float* lse, int B, int Hq, int Hkv, int T, int S, int d_h,
+                                    int causal, float q_scale, float k_scale, float v_scale,
+                                    int64_t pos, void* stream);
+
+/*
  * attn_decode_paged -- one decode step over a block-tabled KV cache ("Self-Attention
  * Complexity, FlashAttention, PagedAttention, and RoPE in Code", Part 3: fixed-size
  * blocks and per-sequence block tables; "Why is attention O(n^2) ...": a decode step

@@ -24,7 +24,7 @@ def lib():
 
 def test_header_declares_entry_points():
     names = header_functions()
-    assert names == sorted(["attn_fwd", "attn_fwd_window", "attn_prefill_paged", "attn_decode_paged",
+    assert names == sorted(["attn_fwd", "attn_fwd_window", "attn_fwd_fp8", "attn_prefill_paged", "attn_decode_paged",
                             "attn_decode_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes",
                             "attn_paged_gather", "attn_status_str"])
 
@@ -122,6 +122,23 @@ def prefill_paged(lib, **kw):
 ])
 def test_prefill_paged_validation(lib, kw, status):
     assert prefill_paged(lib, **kw) == status
+
+
+def fwd_fp8(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, B=1, Hq=4, Hkv=2, T=8, S=8, d=128, causal=1, sq=1.0, sk=1.0,
+             sv=1.0, pos=0)
+    a.update(kw)
+    return lib.attn_fwd_fp8(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["T"], a["S"],
+                            a["d"], a["causal"], a["sq"], a["sk"], a["sv"], a["pos"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(v=None), 1), (dict(out=None), 1), (dict(T=0), 1), (dict(Hq=6, Hkv=4), 1),
+    (dict(causal=2), 1), (dict(sq=0.0), 1), (dict(sk=-1.0), 1), (dict(sv=float("nan")), 1), (dict(sq=float("inf")), 1),
+    (dict(d=64), 2), (dict(S=10), 2), (dict(v=ctypes.c_void_p(0x1002)), 2), (dict(pos=1 << 41), 2),
+])
+def test_fwd_fp8_validation(lib, kw, status):
+    assert fwd_fp8(lib, **kw) == status
 
 
 def bwd(lib, **kw):

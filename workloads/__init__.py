@@ -77,6 +77,24 @@ def make_bwd_inputs(B, Hq, Hkv, T, S, d_h, dtype="bf16", sigma=1.0, seed=0, **_)
     return q, k, v, do
 
 
+def make_fp8_inputs(B, Hq, Hkv, T, S, d_h, sigma=1.0, seed=0, **_):
+    """fp8 E4M3 inputs with one scale per tensor.  Q [B,Hq,T,d_h], K and V [B,Hkv,S,d_h] drawn
+    as in make_fwd_inputs (fp32 N(0, sigma^2), order Q, K, V); each tensor's scale is its
+    largest magnitude / 448 (the largest E4M3 value), its codes are x / scale rounded to
+    E4M3 (torch.float8_e4m3fn, nearest even); V is stored transposed, [B,Hkv,d_h,S].
+    Returns (q8, k8, vt8) as uint8 CPU tensors and (q_scale, k_scale, v_scale)."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    xs = [torch.randn(shape, generator=g, dtype=torch.float32) * sigma
+          for shape in ((B, Hq, T, d_h), (B, Hkv, S, d_h), (B, Hkv, S, d_h))]
+    xs[2] = xs[2].transpose(-1, -2).contiguous()
+    codes, scales = [], []
+    for x in xs:
+        sc = float(x.abs().max()) / 448.0
+        codes.append((x / sc).to(torch.float8_e4m3fn).view(torch.uint8))
+        scales.append(sc)
+    return tuple(codes), tuple(scales)
+
+
 def make_decode_inputs(num_seqs, Hq, Hkv, d_h, block_size=16, len_lo=512, len_hi=8192,
                        dtype="bf16", sigma=1.0, seed=0, seq_lens=None, device=None, **_):
     """Paged KV cache for one decode step.
@@ -217,6 +235,6 @@ def scaled(cfg, **overrides):
     return c
 
 
-__all__ = ["CONFIGS", "make_fwd_inputs", "make_bwd_inputs", "make_decode_inputs", "make_prefill_paged_inputs",
+__all__ = ["CONFIGS", "make_fwd_inputs", "make_bwd_inputs", "make_fp8_inputs", "make_decode_inputs", "make_prefill_paged_inputs",
            "fwd_flops", "bwd_flops", "window_flops", "prefill_paged_flops", "decode_kv_bytes",
            "fwd_io_bytes", "scaled", "torch_dtype"]
