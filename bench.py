@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0          # HBM3E
+PEAK_FP8_TFLOPS = 5033.2       # dense fp8 (E4M3) MFMA: twice the bf16 rate
 
 
 def kernel_sources_digest(files):
@@ -99,6 +100,7 @@ def summarize_pmc(fetch_csv, write_csv, out_dir, extra_kind=None):
                            "fetch_scale": f_scale, "write_scale": w_scale}}
     kinds = (((extra_kind, ["bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"], BWD_SOURCES),)
              if extra_kind == "bwd" else
+             ((extra_kind, ["fwd_fp8_kernel"], FP8_SOURCES),) if extra_kind == "fp8" else
              ((extra_kind, ["fwd_bf16_kernel"], PREFILL_SOURCES),) if extra_kind else
              (("prefill", ["fwd_bf16_kernel"], PREFILL_SOURCES),
               ("decode", ["decode_partial_kernel", "decode_merge_kernel"], DECODE_SOURCES)))
@@ -386,6 +388,76 @@ def bwd_bench(a):
     print(json.dumps(res), flush=True)
 
 
+FP8_SOURCES = ["exact_transformer_attention_amd/csrc/fwd_fp8.hip",
+               "exact_transformer_attention_amd/csrc/attn_common.h",
+               "exact_transformer_attention_amd/csrc/fwd_params.h"]
+
+
+def fp8_bench(a):
+    """fp8 (E4M3) prefill on the causal 8192-token GQA shape (one JSON line)."""
+    import torch
+    import workloads
+    from exact_transformer_attention_amd import attn_fwd_fp8
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS["gqa8k"]
+    (q8, k8, vt8), sc = workloads.make_fp8_inputs(**cfg)
+    q8, k8, vt8 = q8.to(dev), k8.to(dev), vt8.to(dev)
+    out = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=dev)
+
+    def run():
+        attn_fwd_fp8(q8, k8, vt8, *sc, causal=True, pos=0, out=out, lse=lse)
+
+    for _ in range(a.warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    avg = sum(ms) / len(ms)
+    assert bool(torch.isfinite(out).all())
+    if a.copy_calibration:
+        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+    flops = workloads.fwd_flops(**cfg)
+    tf = flops / (avg * 1e-3) / 1e12
+    res = {
+        "metric": "fp8 attention fwd TFLOP/s + % fp8 MFMA peak",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(avg, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8", "data": "synthetic (seeded iid normal, per-tensor amax scaling to E4M3)",
+        "config": {"workload": "causal GQA prefill B=2 Hq=32 Hkv=8 T=S=8192 d_h=128, E4M3 q/k/v (V transposed), "
+                               "inputs taken as already rotated", "scales": [round(x, 8) for x in sc]},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "traffic": measured_traffic("fp8", kernel_sources_digest(FP8_SOURCES)),
+                     "kernel": "fwd_fp8_kernel<4>", "flop_per_launch": flops, "avg_launch_ms": round(avg, 4)},
+    }
+    if not a.no_cpu_baseline:
+        import oracle
+        print("[bench] timing the oracle on the host (fp8 sample)", file=sys.stderr, flush=True)
+        n_kv = 4
+        nq = n_kv * (cfg["Hq"] // cfg["Hkv"])
+        qh, kh, vh = workloads.make_fp8_inputs(**cfg)[0]
+        t0 = time.perf_counter()
+        oracle.attention_fp8(qh[:1, :nq].numpy(), kh[:1, :n_kv].numpy(), vh[:1, :n_kv].numpy(), *sc, causal=True)
+        dt = time.perf_counter() - t0
+        sf = workloads.fwd_flops(1, nq, cfg["T"], cfg["S"], cfg["d_h"], True)
+        res["cpu_baseline"] = dict(value=sf / dt / 1e12, unit="TFLOP/s", cores=cpu_threads(), kind="oracle",
+                                   seconds=round(dt, 3),
+                                   sample=f"batch 0, query heads 0-{nq - 1} (KV heads 0-{n_kv - 1}), all {cfg['T']} rows, "
+                                          f"fp64 numpy on the decoded fp8 values; {sf:.3e} algorithmic FLOP")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -394,11 +466,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "decode", "window", "prefix", "bwd"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "window", "prefix", "bwd", "fp8"], default=None,
                     help="time only one part (profiling runs); 'window' times the causal sliding-window "
                          "prefill (attn_fwd_window) on the same 8192-token GQA workload instead; 'prefix' "
                          "the paged prefill (attn_prefill_paged) of 8 sequences over a shared 6144-token prefix; "
-                         "'bwd' the backward (attn_bwd) of the 8192-token GQA prefill")
+                         "'bwd' the backward (attn_bwd) of the 8192-token GQA prefill; 'fp8' the fp8 prefill "
+                         "(attn_fwd_fp8) on the same shape")
     ap.add_argument("--window", type=int, default=4096, help="window of --only window (keys)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/traffic.json "
@@ -406,7 +479,7 @@ def main():
     a = ap.parse_args()
     if a.traffic_from:
         print(json.dumps(summarize_pmc(a.traffic_from[0], a.traffic_from[1], os.path.join(ROOT, "profiles"),
-                                       extra_kind=a.only if a.only in ("window", "prefix", "bwd") else None),
+                                       extra_kind=a.only if a.only in ("window", "prefix", "bwd", "fp8") else None),
                          indent=1))
         return
     if a.gpus != 1:
@@ -422,6 +495,9 @@ def main():
         return
     if a.only == "bwd":
         bwd_bench(a)
+        return
+    if a.only == "fp8":
+        fp8_bench(a)
         return
 
     import torch
