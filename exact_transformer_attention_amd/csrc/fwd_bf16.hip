@@ -272,7 +272,7 @@ void fwd_bf16_kernel(FwdParams p) {
   };
   // Rotate this thread's raw K chunks of block `tile` into Ks[tile & 1].  The caller has
   // waited for the loads of that block.
-  auto rotate_k = [&](int tile, auto kbc) {
+  auto rotate_k = [&](int tile, auto kbc, const u32x4 (&raw_in)[C::NCH]) {
     constexpr int kb = decltype(kbc)::value;  // == tile & 1
     if constexpr (ROTK) {
       float c[4], s[4];
@@ -283,7 +283,7 @@ void fwd_bf16_kernel(FwdParams p) {
       }
 #pragma unroll
       for (int j = 0; j < C::NCH; ++j) {
-        const u32x4 raw = Kraw[kb][(wid * C::NCH + j) * kWave + lane];
+        const u32x4 raw = raw_in[j];
         u32x4 out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -298,8 +298,7 @@ void fwd_bf16_kernel(FwdParams p) {
     } else {
 #pragma unroll
       for (int j = 0; j < C::NCH; ++j)
-        *(u32x4*)&Ks[kb][(row0 + j * C::RSTEP) * C::KSTR + slot * 8] =
-            Kraw[kb][(wid * C::NCH + j) * kWave + lane];
+        *(u32x4*)&Ks[kb][(row0 + j * C::RSTEP) * C::KSTR + slot * 8] = raw_in[j];
     }
   };
   // Exact angles of this thread's first key of block `tile` (every kResync blocks; the
@@ -366,7 +365,7 @@ void fwd_bf16_kernel(FwdParams p) {
   // rotation's vector instructions run while the matrix cores work on that k-step
   // (the K chunks this thread rotates per block, D / 64 of them with 4 pairs each, make
   // exactly D / 16 units, one per k-step).
-  auto qk_rot = [&](const __bf16* kb, f32x16 (&s)[2][kNB], auto kbc) {
+  auto qk_rot = [&](const __bf16* kb, f32x16 (&s)[2][kNB], auto kbc, const u32x4 (&raw)[C::NCH]) {
     constexpr int kn = decltype(kbc)::value;  // buffer of the block being rotated
     static_assert(C::NCH * 4 == C::KS, "one rotation unit per k-step");
 #pragma unroll
@@ -381,9 +380,7 @@ void fwd_bf16_kernel(FwdParams p) {
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
         s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_op, bop, acc, 0, 0, 0);
       }
-    u32x4 raw[C::NCH], out[C::NCH];
-#pragma unroll
-    for (int j = 0; j < C::NCH; ++j) raw[j] = Kraw[kn][(wid * C::NCH + j) * kWave + lane];
+    u32x4 out[C::NCH];
     float c[4], sn[4];
     if constexpr (ROTK) {
 #pragma unroll
@@ -479,7 +476,13 @@ void fwd_bf16_kernel(FwdParams p) {
   auto step = [&](auto par, int it) {
     constexpr int PAR = decltype(par)::value;
     __syncthreads();  // block it is rotated and landed; everyone is done with block it-1
-    if (it + 2 < n_tiles) load_k(it + 2);
+    // This thread's raw K chunks of block it+1 are read before any load is issued, and raw
+    // K of block it+2 is only requested once the product of block it has read its
+    // operands: the compiler cannot tell the LDS buffers apart and would otherwise wait
+    // for the loads in flight to land before those reads.
+    u32x4 raw[C::NCH];
+#pragma unroll
+    for (int j = 0; j < C::NCH; ++j) raw[j] = Kraw[PAR ^ 1][(wid * C::NCH + j) * kWave + lane];
     if (it + 1 < n_tiles) load_v(it + 1);
     const bool rot = it + 1 < n_tiles;  // rotate block it+1 during this iteration
     if (rot) resync(it + 1);
@@ -490,7 +493,8 @@ void fwd_bf16_kernel(FwdParams p) {
       f32x16 s[2][kNB];
       // The rotation of block it+1 is woven into the product; after the last block it
       // rotates stale data into a buffer nobody reads.
-      qk_rot(kbuf, s, std::integral_constant<int, PAR ^ 1>{});
+      qk_rot(kbuf, s, std::integral_constant<int, PAR ^ 1>{}, raw);
+      if (it + 2 < n_tiles) load_k(it + 2);
       // mask (diagonal / tail blocks only)
       const bool need_mask = (k0 + kBN > S) || (p.causal && (int64_t)(k0 + kBN - 1) > pos + wrow0) ||
                              (p.window > 0 && (int64_t)k0 < lo_wave + kQW - 1);
@@ -556,8 +560,9 @@ void fwd_bf16_kernel(FwdParams p) {
         pv(vbuf, 2 * mb, pop);
         pv(vbuf, 2 * mb + 1, pop);
       }
-    } else if (rot) {
-      rotate_k(it + 1, std::integral_constant<int, PAR ^ 1>{});
+    } else {
+      if (rot) rotate_k(it + 1, std::integral_constant<int, PAR ^ 1>{}, raw);
+      if (it + 2 < n_tiles) load_k(it + 2);
     }
     wait_loads();  // this thread's loads issued above have landed before the next barrier
   };
@@ -570,8 +575,11 @@ void fwd_bf16_kernel(FwdParams p) {
     if (it0 + 1 < n_tiles) load_k(it0 + 1);
     wait_loads();
     resync(it0, true);
-    if (it0 & 1) rotate_k(it0, std::integral_constant<int, 1>{});
-    else rotate_k(it0, std::integral_constant<int, 0>{});
+    u32x4 raw[C::NCH];
+#pragma unroll
+    for (int j = 0; j < C::NCH; ++j) raw[j] = Kraw[it0 & 1][(wid * C::NCH + j) * kWave + lane];
+    if (it0 & 1) rotate_k(it0, std::integral_constant<int, 1>{}, raw);
+    else rotate_k(it0, std::integral_constant<int, 0>{}, raw);
   }
   int it = it0;
   if (it < n_tiles && (it & 1)) step(std::integral_constant<int, 1>{}, it++);
