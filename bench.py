@@ -105,10 +105,10 @@ def summarize_pmc(fetch_csv, write_csv, out_dir, extra_kind=None):
              (("prefill", ["fwd_bf16_kernel"], PREFILL_SOURCES),
               ("decode", ["decode_partial_kernel", "decode_merge_kernel"], DECODE_SOURCES)))
     path = os.path.join(out_dir, "traffic.json")
-    if extra_kind and os.path.exists(path):  # a window or prefix run adds its entry to the main one
+    if os.path.exists(path):  # entries of the other runs are kept
         with open(path) as f:
             old = json.load(f)
-        old[extra_kind + "_calibration"] = res["calibration"]
+        old[(extra_kind + "_calibration") if extra_kind else "calibration"] = res["calibration"]
         res = old
     for kind, keys, srcs in kinds:
         fb = [pick(fetch, k) for k in keys]
