@@ -199,11 +199,8 @@ void fwd_fp8_kernel(FwdParams p) {
         s[mb] = mfma_fp8(cat8(lo, hi), qop[ks], s[mb]);
       }
     }
-    // base-2 logits; hidden keys -inf (diagonal and tail blocks only)
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[mb][r] *= c2;
+    // hidden keys -inf (diagonal and tail blocks only); the base-2 scale c2 is applied in
+    // the exponent below
     const bool need_mask = (k0 + kBlk > S) || (p.causal && (int64_t)(k0 + kBlk - 1) > pos + wrow0);
     if (need_mask) {
       const int64_t lim = pos + t;
@@ -223,13 +220,12 @@ void fwd_fp8_kernel(FwdParams p) {
       const float bias = (m_ref == -INFINITY) ? 0.f : m_ref;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        float sum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pr[mb][r] = fast_exp2(s[mb][r] - bias);
-          sum += pr[mb][r];
-        }
-        lt[mb] = sum;
+        for (int r = 0; r < 16; ++r) pr[mb][r] = fast_exp2(fmaf(s[mb][r], c2, -bias));
+        float q4[4];  // four partial sums: short dependency chains
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q4[k] = (pr[mb][k] + pr[mb][k + 4]) + (pr[mb][k + 8] + pr[mb][k + 12]);
+        lt[mb] = (q4[0] + q4[1]) + (q4[2] + q4[3]);
       }
     };
     expo();
@@ -241,7 +237,7 @@ void fwd_fp8_kernel(FwdParams p) {
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c2;  // c2 > 0: the max of the scaled logits
       // raised only when the max is more than 2^3 above it: every p stays <= 8, so a lane's
       // 16-key half sums to <= 128 < kPMax and the check does not fire again for it
       const bool need = tmax > m_ref + 3.f;
