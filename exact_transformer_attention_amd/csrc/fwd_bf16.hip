@@ -42,7 +42,8 @@
 //    block by angle addition and are re-derived exactly (fp64 reduction) every 16 blocks.
 //  * Raw K is loaded two blocks ahead and V one block ahead; the rotation of block j+1
 //    happens during block j.  Work is ordered longest-first for causal load balance and
-//    mapped so all query blocks of one KV head land on one XCD (shared L2).
+//    mapped so all query blocks of one KV head land on one XCD, which runs its head groups
+//    one after the other (one group's K/V in its L2 at a time).
 #include <math.h>
 
 #include <type_traits>
@@ -125,9 +126,11 @@ void fwd_bf16_kernel(FwdParams p) {
   {
     const int bid = blockIdx.x;
     if (p.xcd_remap) {
-      const int xcd = bid % 8, slot = bid / 8, gpx = p.n_groups / 8;
-      qb = p.n_qblocks - 1 - slot / gpx;
-      grp = xcd + 8 * (slot % gpx);
+      // an XCD runs its head groups one after the other, so one group's K/V is what its
+      // L2 holds at a time
+      const int xcd = bid % 8, slot = bid / 8;
+      qb = p.n_qblocks - 1 - slot % p.n_qblocks;
+      grp = xcd + 8 * (slot / p.n_qblocks);
     } else {
       qb = p.n_qblocks - 1 - bid / p.n_groups;
       grp = bid % p.n_groups;

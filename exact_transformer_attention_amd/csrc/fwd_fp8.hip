@@ -92,9 +92,11 @@ void fwd_fp8_kernel(FwdParams p) {
   {
     const int bid = blockIdx.x;
     if (p.xcd_remap) {
-      const int xcd = bid % 8, slot = bid / 8, gpx = p.n_groups / 8;
-      qb = p.n_qblocks - 1 - slot / gpx;
-      grp = xcd + 8 * (slot % gpx);
+      // an XCD runs its head groups one after the other, so one group's K/V is what its
+      // L2 holds at a time
+      const int xcd = bid % 8, slot = bid / 8;
+      qb = p.n_qblocks - 1 - slot % p.n_qblocks;
+      grp = xcd + 8 * (slot / p.n_qblocks);
     } else {
       qb = p.n_qblocks - 1 - bid / p.n_groups;
       grp = bid % p.n_groups;
