@@ -90,4 +90,31 @@ __device__ __forceinline__ float rope_turns(int64_t p, double c) {
   return (float)a;
 }
 
+
+// Work order of a grid of n_groups x nblk workgroups, block-major rank 0 = the work item
+// to start first.  Workgroup bid runs on XCD bid % 8, so with mode != 0 (n_groups a
+// multiple of 8) all items of a group go to one XCD (one L2).  Mode 1: the XCD interleaves
+// its groups, all items in rank order (longest first when rank 0 is the longest).  Mode 2:
+// the XCD runs its groups one after the other, so its L2 holds one group's K/V at a time;
+// the host picks it only when each group has enough items (nblk >= kSeqOrderMin) for the
+// next group's long items to start early enough.
+constexpr int kSeqOrderMin = 64;
+__device__ __forceinline__ void work_order(int bid, int nblk, int n_groups, int mode, int& rank, int& grp) {
+  if (mode == 2) {
+    const int xcd = bid % 8, slot = bid / 8;
+    rank = slot % nblk;
+    grp = xcd + 8 * (slot / nblk);
+  } else if (mode == 1) {
+    const int xcd = bid % 8, slot = bid / 8, gpx = n_groups / 8;
+    rank = slot / gpx;
+    grp = xcd + 8 * (slot % gpx);
+  } else {
+    rank = bid / n_groups;
+    grp = bid % n_groups;
+  }
+}
+__host__ __device__ constexpr int work_order_mode(int nblk, int n_groups) {
+  return (n_groups % 8) ? 0 : (nblk >= kSeqOrderMin ? 2 : 1);
+}
+
 }  // namespace attn

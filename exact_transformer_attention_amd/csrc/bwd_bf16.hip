@@ -205,19 +205,11 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
 
   // ---- work item: (batch, KV head, 128-key block).  Key blocks run in increasing order
   // (for causal attention the first blocks see the most queries); all blocks of one KV
-  // head stay on one XCD so its q' / dO tiles are shared through that XCD's L2.
+  // head stay on one XCD so its q' / dO tiles are shared through that XCD's L2
+  // (work_order).
   int kb, grp;
   {
-    const int bid = blockIdx.x;
-    if (p.xcd_remap) {
-      // an XCD runs its KV heads one after the other (their q' / dO tiles in its L2)
-      const int xcd = bid % 8, slot = bid / 8;
-      kb = slot % p.n_kblocks;
-      grp = xcd + 8 * (slot / p.n_kblocks);
-    } else {
-      kb = bid / p.n_groups;
-      grp = bid % p.n_groups;
-    }
+    work_order(blockIdx.x, p.n_kblocks, p.n_groups, p.xcd_remap, kb, grp);
   }
   const int b = grp / p.Hkv, kvh = grp % p.Hkv;
   const int G = p.Hq / p.Hkv;
@@ -503,21 +495,14 @@ void bwd_dq_kernel(BwdParams p) {
   const int g = lane / 32;
 
   // ---- work item: (batch, head group, query block), longest causal blocks first, all
-  // blocks of one head group on one XCD.
+  // blocks of one head group on one XCD (work_order).
   constexpr int RH = kQW * 32 / HP;  // rows per head per workgroup
   int qb, grp;
   {
     const int bid = blockIdx.x;
-    if (p.xcd_remap) {
-      // an XCD runs its head groups one after the other, so one group's K/V is what its
-      // L2 holds at a time
-      const int xcd = bid % 8, slot = bid / 8;
-      qb = p.n_qblocks - 1 - slot % p.n_qblocks;
-      grp = xcd + 8 * (slot / p.n_qblocks);
-    } else {
-      qb = p.n_qblocks - 1 - bid / p.n_groups;
-      grp = bid % p.n_groups;
-    }
+    int rank;
+    work_order(bid, p.n_qblocks, p.n_groups, p.xcd_remap, rank, grp);
+    qb = p.n_qblocks - 1 - rank;
   }
   const int hpg = p.Hq / HP;
   const int b = grp / hpg;
@@ -713,7 +698,7 @@ hipError_t launch_dq(BwdParams p, hipStream_t stream) {
   constexpr int RH = kQW * 32 / HP;
   p.n_qblocks = (p.T + RH - 1) / RH;
   p.n_groups = p.B * (p.Hq / HP);
-  p.xcd_remap = (p.n_groups % 8) == 0;
+  p.xcd_remap = work_order_mode(p.n_qblocks, p.n_groups);
   const long long grid = (long long)p.n_qblocks * p.n_groups;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_dq_kernel<HP>), dim3((unsigned)grid), dim3(kQThreads), 0, stream, p);
@@ -733,7 +718,7 @@ hipError_t launch_bwd_bf16(BwdParams p, hipStream_t stream) {
   BwdParams kv = p;
   kv.n_kblocks = (p.S + kKeysPerWG - 1) / kKeysPerWG;
   kv.n_groups = p.B * p.Hkv;
-  kv.xcd_remap = (kv.n_groups % 8) == 0;
+  kv.xcd_remap = work_order_mode(kv.n_kblocks, kv.n_groups);
   grid = (long long)kv.n_kblocks * kv.n_groups;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)grid), dim3(kKVThreads), 0, stream, kv);

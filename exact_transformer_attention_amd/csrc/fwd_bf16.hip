@@ -42,8 +42,9 @@
 //    block by angle addition and are re-derived exactly (fp64 reduction) every 16 blocks.
 //  * Raw K is loaded two blocks ahead and V one block ahead; the rotation of block j+1
 //    happens during block j.  Work is ordered longest-first for causal load balance and
-//    mapped so all query blocks of one KV head land on one XCD, which runs its head groups
-//    one after the other (one group's K/V in its L2 at a time).
+//    mapped so all query blocks of one KV head land on one XCD; with enough query blocks
+//    per group the XCD runs its groups one after the other (one group's K/V in its L2 at
+//    a time), else it interleaves them longest first (work_order).
 #include <math.h>
 
 #include <type_traits>
@@ -120,21 +121,15 @@ void fwd_bf16_kernel(FwdParams p) {
   const int l32 = lane % 32;
   const int g = lane / 32;
 
-  // ---- work item: (batch, head group, query block), longest causal blocks first.
+  // ---- work item: (batch, head group, query block), longest causal blocks first, all
+  // blocks of one head group on one XCD (work_order).
   constexpr int RH = kNW * kQW / HP;  // rows per head per workgroup
   int qb, grp;
   {
     const int bid = blockIdx.x;
-    if (p.xcd_remap) {
-      // an XCD runs its head groups one after the other, so one group's K/V is what its
-      // L2 holds at a time
-      const int xcd = bid % 8, slot = bid / 8;
-      qb = p.n_qblocks - 1 - slot % p.n_qblocks;
-      grp = xcd + 8 * (slot / p.n_qblocks);
-    } else {
-      qb = p.n_qblocks - 1 - bid / p.n_groups;
-      grp = bid % p.n_groups;
-    }
+    int rank;
+    work_order(bid, p.n_qblocks, p.n_groups, p.xcd_remap, rank, grp);
+    qb = p.n_qblocks - 1 - rank;
   }
   const int hpg = p.Hq / HP;
   const int b = grp / hpg;
@@ -621,7 +616,7 @@ hipError_t launch_one(FwdParams q, hipStream_t stream) {
   constexpr int RH = kNW * kQW / HP;
   q.n_qblocks = (q.T + RH - 1) / RH;
   q.n_groups = q.B * (q.Hq / HP);
-  q.xcd_remap = (q.n_groups % 8) == 0;
+  q.xcd_remap = work_order_mode(q.n_qblocks, q.n_groups);
   const long long grid = (long long)q.n_qblocks * q.n_groups;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, HP, ROPE, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, q);

@@ -86,21 +86,14 @@ void fwd_fp8_kernel(FwdParams p) {
   const int g = lane / 32;
 
   // ---- work item: (batch, head group, query block), longest causal blocks first, all
-  // blocks of one head group on one XCD.
+  // blocks of one head group on one XCD (work_order).
   constexpr int RH = kW8 * 32 / HP;  // rows per head per workgroup
   int qb, grp;
   {
     const int bid = blockIdx.x;
-    if (p.xcd_remap) {
-      // an XCD runs its head groups one after the other, so one group's K/V is what its
-      // L2 holds at a time
-      const int xcd = bid % 8, slot = bid / 8;
-      qb = p.n_qblocks - 1 - slot % p.n_qblocks;
-      grp = xcd + 8 * (slot / p.n_qblocks);
-    } else {
-      qb = p.n_qblocks - 1 - bid / p.n_groups;
-      grp = bid % p.n_groups;
-    }
+    int rank;
+    work_order(bid, p.n_qblocks, p.n_groups, p.xcd_remap, rank, grp);
+    qb = p.n_qblocks - 1 - rank;
   }
   const int hpg = p.Hq / HP;
   const int b = grp / hpg;
@@ -311,7 +304,7 @@ hipError_t launch_fp8_one(FwdParams q, hipStream_t stream) {
   constexpr int RH = kW8 * 32 / HP;
   q.n_qblocks = (q.T + RH - 1) / RH;
   q.n_groups = q.B * (q.Hq / HP);
-  q.xcd_remap = (q.n_groups % 8) == 0;
+  q.xcd_remap = work_order_mode(q.n_qblocks, q.n_groups);
   const long long grid = (long long)q.n_qblocks * q.n_groups;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fwd_fp8_kernel<HP>), dim3((unsigned)grid), dim3(kThr8), 0, stream, q);

@@ -27,7 +27,7 @@ struct FwdParams {
   int num_blocks;
   int n_qblocks;  // query blocks per (batch, head group)
   int n_groups;   // batch * head groups
-  int xcd_remap;  // 1 if n_groups is a multiple of 8 (see work mapping in the kernel)
+  int xcd_remap;  // work order mode (work_order in attn_common.h)
   int64_t pos;
   float q_scale, k_scale, v_scale;  // fp8 prefill: value = code * scale
   // RoPE: rope_c[i] = rope_base^(-2i/d_h) / (2 pi), i = 0..d_h/2-1 (turns per position).
