@@ -170,35 +170,28 @@ void fwd_bf16_kernel(FwdParams p) {
   }
 
   // ---- Q^T operand in registers: lane holds query l32 of n-block nb, dims ks*16 + g*8.
+  // Only the raw rows are loaded here (with the RoPE frequencies, staged in LDS); the
+  // rotation and scaling run in the prologue below, while the first K/V blocks are in
+  // flight.
   bf16x8 qop[kNB][C::KS];
-  {
-    const float qscale = kLog2e / sqrtf((float)D);
+  u32x4 qraw[kNB][C::KS];
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      const int t = wrow0 + nb * 32 + l32;
-      const bool ok = t < T;
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int t = wrow0 + nb * 32 + l32;
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (ok) raw = *(const u32x4*)(qg + (size_t)t * D + ks * 16 + g * 8);
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x0 = bf16_lo(raw[e]), x1 = bf16_hi(raw[e]);
-          if constexpr (ROPE) {
-            const float tr = rope_turns(pos + t, p.rope_c[ks * 8 + g * 4 + e]);
-            float sn, cs;
-            sincos_rev(tr, &sn, &cs);
-            const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
-            x0 = y0;
-            x1 = y1;
-          }
-          pk[e] = pack_bf16(x0 * qscale, x1 * qscale);
-        }
-        qop[nb][ks] = __builtin_bit_cast(bf16x8, pk);
-      }
+    for (int ks = 0; ks < C::KS; ++ks) {
+      qraw[nb][ks] = (u32x4){0u, 0u, 0u, 0u};
+      if (t < T) qraw[nb][ks] = *(const u32x4*)(qg + (size_t)t * D + ks * 16 + g * 8);
     }
   }
+  __shared__ double ropec_s[ROPE ? D / 2 : 1];
+  if constexpr (ROPE) {
+    if (tid < D / 2) ropec_s[tid] = p.rope_c[tid];
+  }
+  // Q rows landed before the K/V blocks are requested: a later wait for them would also
+  // wait for those blocks
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  if constexpr (ROPE) __syncthreads();
   // Extra k-step: K side holds 1 in slot 0 of the g = 0 lanes, Q side holds -m there.
   const bf16x8 ones_op = __builtin_bit_cast(bf16x8, (u32x4){g == 0 ? 0x3f80u : 0u, 0u, 0u, 0u});
 
@@ -213,7 +206,7 @@ void fwd_bf16_kernel(FwdParams p) {
   if constexpr (ROTK) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      cturn[e] = p.rope_c[slot * 4 + e];
+      cturn[e] = ropec_s[slot * 4 + e];
       sincos_rev(rope_turns((int64_t)C::RSTEP, cturn[e]), &rs[e], &rc[e]);
       sincos_rev(rope_turns((int64_t)kBN, cturn[e]), &ts[e], &tc[e]);
     }
@@ -571,8 +564,41 @@ void fwd_bf16_kernel(FwdParams p) {
     load_k(it0);
     load_v(it0);
     if (it0 + 1 < n_tiles) load_k(it0 + 1);
-    wait_loads();
+  }
+  {  // Q: RoPE at its positions and the scale log2(e)/sqrt(d_h), folded into the operand
+    const float qscale = kLog2e / sqrtf((float)D);
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int t = wrow0 + nb * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x0 = bf16_lo(qraw[nb][ks][e]), x1 = bf16_hi(qraw[nb][ks][e]);
+          if constexpr (ROPE) {
+            const float tr = rope_turns(pos + t, ropec_s[ks * 8 + g * 4 + e]);
+            float sn, cs;
+            sincos_rev(tr, &sn, &cs);
+            const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+            x0 = y0;
+            x1 = y1;
+          }
+          pk[e] = pack_bf16(x0 * qscale, x1 * qscale);
+        }
+        qop[nb][ks] = __builtin_bit_cast(bf16x8, pk);
+      }
+    }
+  }
+  // the Q operand is complete before the wait for the first blocks (its arithmetic hides
+  // their latency; without a use here the compiler would sink it below the wait)
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) asm volatile("" ::"v"(qop[nb][ks]));
+  if (it0 < n_tiles) {
     resync(it0, true);
+    wait_loads();
     u32x4 raw[C::NCH];
 #pragma unroll
     for (int j = 0; j < C::NCH; ++j) raw[j] = Kraw[it0 & 1][(wid * C::NCH + j) * kWave + lane];
