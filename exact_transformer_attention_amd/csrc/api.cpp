@@ -23,6 +23,10 @@ void fill_rope(double* c, int d_h, float base) {
 
 bool bad_base(float rope_base) { return !(std::isfinite(rope_base) && rope_base >= 0.f); }
 
+// The kernels move 16-byte chunks of every head-row tensor and 4-byte words of the lse and
+// block tables; misaligned pointers are rejected rather than read.
+bool misaligned(const void* p, uintptr_t a) { return p && ((uintptr_t)p & (a - 1)) != 0; }
+
 }  // namespace
 
 extern "C" {
@@ -46,6 +50,8 @@ attn_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, f
                        int T, int S, int d_h, int causal, int64_t window, float rope_base, int64_t pos,
                        attn_dtype_t dtype, void* stream) {
   if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) || misaligned(lse, 4))
+    return ATTN_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || d_h < 1) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
@@ -99,6 +105,8 @@ attn_status_t attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void
                            int Hkv, int T, int S, int d_h, int causal, float q_scale, float k_scale, float v_scale,
                            int64_t pos, void* stream) {
   if (!q8 || !k8 || !vt8 || !out) return ATTN_ERR_INVALID_ARG;
+  if (misaligned(q8, 16) || misaligned(k8, 16) || misaligned(out, 16) || misaligned(lse, 4))
+    return ATTN_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || d_h < 1) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
@@ -135,6 +143,9 @@ attn_status_t attn_prefill_paged(const void* q, const void* k_cache, const void*
                                  int num_blocks, float rope_base, void* out, float* lse, attn_dtype_t dtype,
                                  void* stream) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return ATTN_ERR_INVALID_ARG;
+  if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(out, 16) ||
+      misaligned(lse, 4) || misaligned(block_table, 4) || misaligned(seq_lens, 4))
+    return ATTN_ERR_INVALID_ARG;
   if (num_seqs < 1 || Hq < 1 || Hkv < 1 || d_h < 1 || T < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
       block_size < 1)
     return ATTN_ERR_INVALID_ARG;
@@ -196,6 +207,9 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        int d_h, int causal, int64_t window, float rope_base, int64_t pos, void* workspace,
                        size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
+  for (const void* t : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv, (const void*)workspace})
+    if (misaligned(t, 16)) return ATTN_ERR_INVALID_ARG;
+  if (misaligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
   if (!bwd_sizes_ok(B, Hq, Hkv, T, S, d_h)) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && causal != 1)) return ATTN_ERR_INVALID_ARG;
@@ -255,6 +269,9 @@ attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* 
                                 int num_blocks, float rope_base, void* out, float* lse, void* workspace,
                                 size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return ATTN_ERR_INVALID_ARG;
+  if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(out, 16) ||
+      misaligned(lse, 4) || misaligned(block_table, 4) || misaligned(seq_lens, 4))
+    return ATTN_ERR_INVALID_ARG;
   if (num_seqs < 1 || Hq < 1 || Hkv < 1 || d_h < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
       block_size < 1)
     return ATTN_ERR_INVALID_ARG;
@@ -266,6 +283,7 @@ attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* 
     return ATTN_ERR_UNSUPPORTED;
   const size_t need = attn_decode_workspace_bytes(num_seqs, Hq, Hkv, d_h, max_blocks_per_seq, block_size);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (misaligned(workspace, 16)) return ATTN_ERR_INVALID_ARG;
 
   attn::DecodeParams p;
   std::memset(&p, 0, sizeof(p));
@@ -296,6 +314,8 @@ attn_status_t attn_paged_gather(const void* cache, const int32_t* block_table, c
                                 int block_size, int num_seqs, int Hkv, int d_h, int max_blocks_per_seq,
                                 int num_blocks, int elem_bytes, void* dst, void* stream) {
   if (!cache || !block_table || !seq_lens || !dst) return ATTN_ERR_INVALID_ARG;
+  if (misaligned(cache, 4) || misaligned(dst, 4) || misaligned(block_table, 4) || misaligned(seq_lens, 4))
+    return ATTN_ERR_INVALID_ARG;
   if (num_seqs < 1 || Hkv < 1 || d_h < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || block_size < 1)
     return ATTN_ERR_INVALID_ARG;
   if (elem_bytes != 2 && elem_bytes != 4) return ATTN_ERR_INVALID_ARG;

@@ -16,6 +16,10 @@
  *            block_table [num_seqs, max_blocks_per_seq] int32;  seq_lens [num_seqs] int32;
  *            lse [num_seqs, Hq] fp32
  * out has the dtype of the inputs; accumulation and lse are fp32.
+ * Alignment: tensors of head rows (q, k, v, out, their gradients, the caches and the
+ * workspaces) start on 16-byte boundaries, lse, block tables and sequence lengths on
+ * 4-byte ones (the gather's cache and destination on 4-byte ones); otherwise the call
+ * returns ATTN_ERR_INVALID_ARG.
  */
 #ifndef LIBATTN_ATTN_H
 #define LIBATTN_ATTN_H

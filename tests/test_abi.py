@@ -192,3 +192,12 @@ def test_gather_validation(lib):
     assert f(None, FAKE, FAKE, 16, 1, 1, 128, 1, 1, 2, FAKE, None) == 1
     assert f(FAKE, FAKE, FAKE, 16, 1, 1, 128, 1, 1, 3, FAKE, None) == 1
     assert f(FAKE, FAKE, FAKE, 8, 1, 1, 128, 1, 1, 2, FAKE, None) == 2
+
+
+def test_misaligned_pointers_rejected(lib):
+    import exact_transformer_attention_amd as e
+    odd = ctypes.c_void_p(0x1002)   # 2-byte aligned: a bf16 view one element in
+    assert fwd(lib, q=odd) == e.ATTN_ERR_INVALID_ARG
+    assert fwd(lib, out=odd) == e.ATTN_ERR_INVALID_ARG
+    assert fwd(lib, lse=ctypes.c_void_p(0x1002)) == e.ATTN_ERR_INVALID_ARG
+    assert fwd(lib, k=ctypes.c_void_p(0x1008)) == e.ATTN_ERR_INVALID_ARG
