@@ -320,37 +320,8 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][nb][r] = 0.f;
 
-  // S'^T = K Q^T - m for both 32-key halves and both query n-blocks.
-  auto qk = [&](const __bf16* kb, f32x16 (&s)[2][kNB]) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-        const bf16x8 bop = __builtin_bit_cast(
-            bf16x8, (u32x4){g == 0 ? (__builtin_bit_cast(uint32_t, -bias) >> 16) : 0u, 0u, 0u, 0u});
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-        s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_op, bop, acc, 0, 0, 0);
-      }
-    bf16x8 aop[C::KS][2];
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) aop[ks][mb] = *(const bf16x8*)(kb + (mb * 32 + l32) * C::KSTR + ks * 16 + g * 8);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a = aop[ks][mb];
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
-          s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[nb][ks], s[mb][nb], 0, 0, 0);
-      }
-    }
-  };
-  // The same product with the rotation of the next K block woven in: after each k-step
+  // S'^T = K Q^T - m for both 32-key halves and both query n-blocks (the bias k-step first),
+  // with the rotation of the next K block woven in: after each k-step
   // (its MFMAs issued), one unit of the rotation (one 4-pair slice of one of this
   // thread's chunks).  The scheduling barrier after each slice keeps the order, so the
   // rotation's vector instructions run while the matrix cores work on that k-step
