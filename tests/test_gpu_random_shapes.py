@@ -76,3 +76,53 @@ def test_random_backward(c):
     check_grad(f64(dq), rq, "dq")
     check_grad(f64(dk), rk, "dk")
     check_grad(f64(dv), rv, "dv")
+
+
+def draw_decode_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        ns = int(rng.integers(1, 24))
+        lens = [int(x) for x in rng.integers(1, 2500, ns)]
+        cases.append(dict(num_seqs=ns, Hq=Hkv * G, Hkv=Hkv, seq_lens=lens,
+                          rope_base=float(rng.choice([0.0, 10000.0])), seed=2000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("c", draw_decode_cases(10, seed=20260303),
+                         ids=lambda c: f"{c['num_seqs']}seq-{c['Hq']}/{c['Hkv']}")
+def test_random_decode(c):
+    from exact_transformer_attention_amd import attn_decode_paged
+    say(f"random decode {c}")
+    d = workloads.make_decode_inputs(num_seqs=c["num_seqs"], Hq=c["Hq"], Hkv=c["Hkv"], d_h=128,
+                                     seq_lens=c["seq_lens"], seed=c["seed"])
+    out, lse = attn_decode_paged(d["q"].cuda(), d["k_cache"].cuda(), d["v_cache"].cuda(), d["block_table"].cuda(),
+                                 d["seq_lens"].cuda(), block_size=d["block_size"], rope_base=c["rope_base"])
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(f64(d["q"]), f64(d["k_cache"]), f64(d["v_cache"]), d["block_table"].numpy(),
+                                 d["seq_lens"].numpy(), d["block_size"], rope_base=c["rope_base"])
+    check_close(f64(out), ro, "bf16", "decode", f64(lse), rl)
+
+
+@pytest.mark.parametrize("c", [c for c in draw_fwd_cases(40, seed=20260404) if c["mode"] != "window"][:8],
+                         ids=lambda c: f"{c['mode']}-{c['B']}x{c['Hq']}/{c['Hkv']}-{c['T']}x{c['S']}")
+def test_random_fp8(c):
+    from exact_transformer_attention_amd import attn_fwd_fp8
+    S = (c["S"] + 3) // 4 * 4  # the fp8 path takes S in multiples of 4
+    T = min(c["T"], S)
+    causal = c["mode"] == "causal"
+    say(f"random fp8 {c} (T={T}, S={S})")
+    (q8, k8, vt8), sc = workloads.make_fp8_inputs(B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], T=T, S=S, d_h=128,
+                                                  seed=c["seed"])
+    out, lse = attn_fwd_fp8(q8.cuda(), k8.cuda(), vt8.cuda(), *sc, causal=causal, pos=S - T)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_fp8(q8.numpy(), k8.numpy(), vt8.numpy(), *sc, causal=causal, pos=S - T)
+    from test_gpu_fp8 import LSE_ABS, MAX_REL, REL_RMS
+    got, gl = f64(out), f64(lse)
+    ma, rr = np.abs(got - ro).max(), oracle.rel_rms(got, ro)
+    fin = np.isfinite(rl)
+    le = np.abs(gl[fin] - rl[fin]).max() if fin.any() else 0.0
+    say(f"fp8: max_abs={ma:.3e} rel_rms={rr:.3e} lse={le:.3e}")
+    assert ma <= MAX_REL * np.abs(ro).max() and rr <= REL_RMS and le <= LSE_ABS
