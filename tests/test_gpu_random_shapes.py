@@ -126,3 +126,30 @@ def test_random_fp8(c):
     le = np.abs(gl[fin] - rl[fin]).max() if fin.any() else 0.0
     say(f"fp8: max_abs={ma:.3e} rel_rms={rr:.3e} lse={le:.3e}")
     assert ma <= MAX_REL * np.abs(ro).max() and rr <= REL_RMS and le <= LSE_ABS
+
+
+def draw_paged_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2, 4]))
+        N = int(rng.integers(1, 5))
+        cases.append(dict(N=N, Hq=Hkv * int(rng.choice([1, 2, 4])), Hkv=Hkv, T=int(rng.integers(1, 200)),
+                          P=int(rng.integers(0, 700)), extra=[int(x) for x in rng.integers(0, 150, N)],
+                          rope_base=float(rng.choice([0.0, 10000.0])), seed=3000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("c", draw_paged_cases(8, seed=20260505),
+                         ids=lambda c: f"{c['N']}seq-{c['Hq']}/{c['Hkv']}-T{c['T']}-P{c['P']}")
+def test_random_prefill_paged(c):
+    from exact_transformer_attention_amd import attn_prefill_paged
+    say(f"random paged prefill {c}")
+    d = workloads.make_prefill_paged_inputs(c["N"], c["Hq"], c["Hkv"], 128, c["T"], c["P"], c["extra"],
+                                            seed=c["seed"])
+    out, lse = attn_prefill_paged(d["q"].cuda(), d["k_cache"].cuda(), d["v_cache"].cuda(), d["block_table"].cuda(),
+                                  d["seq_lens"].cuda(), block_size=d["block_size"], rope_base=c["rope_base"])
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_paged(f64(d["q"]), f64(d["k_cache"]), f64(d["v_cache"]), d["block_table"].numpy(),
+                                  d["seq_lens"].numpy(), d["block_size"], rope_base=c["rope_base"])
+    check_close(f64(out), ro, "bf16", "paged prefill", f64(lse), rl)
