@@ -127,3 +127,44 @@ def test_full_workload_every_row_written(name):
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all()), "rows left unwritten"
     assert bool(torch.isfinite(lse).all()), "lse left unwritten"
+
+
+@pytest.mark.parametrize("sigma", [2.0, 3.0])
+def test_bf16_large_logits(sigma):
+    """Inputs with sigma 2-3 spread the logits over tens of units, so the running reference is
+    raised often and by large steps (the rare rescaling path).  The bf16 rounding of the
+    rotated q and k perturbs each logit by ~2^-9 of its size (~sigma^2) and the output by that
+    times |v| (~sigma): the relative RMS bound stays 1e-2, the absolute bounds scale as
+    sigma^2 (lse) and sigma^3 (output)."""
+    cfg = dict(B=1, Hq=4, Hkv=2, T=300, S=300, d_h=128, dtype="bf16", sigma=sigma, seed=31 + int(sigma))
+    say(f"large logits {cfg}")
+    q, k, v = gen(cfg)
+    out, lse = run_fwd_gpu(q, k, v, True, 10000.0, 0)
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), causal=True, rope_base=10000.0)
+    o, l = f64(out), f64(lse)
+    ma, rr, le = oracle.max_abs(o, ro), oracle.rel_rms(o, ro), oracle.max_abs(l, rl)
+    say(f"sigma {sigma}: max_abs={ma:.3e} rel_rms={rr:.3e} lse={le:.3e}")
+    assert rr <= 1e-2 and ma <= 2e-2 * sigma ** 3 and le <= 2e-2 * sigma ** 2
+
+
+def test_bf16_logits_rising_every_block():
+    """Keys whose logits grow along the sequence: every 64-key block holds a new row maximum
+    more than 2^8 above the last one, so the reference is raised in every block.  The logits
+    reach ~68 and are coherent sums (every term of q.k has the same sign), so the bf16 rounding
+    of the scaled q (2^-9 per element, not cancelling) moves lse by up to ~2^-9 of its size: the
+    output keeps the bf16 bounds, lse is held to 2^-8 of its size plus the usual 2e-2."""
+    B, Hq, Hkv, T, S, d = 1, 4, 1, 256, 512, 128
+    g = torch.Generator("cpu").manual_seed(5)
+    u = torch.randn(d, generator=g)
+    q = u.view(1, 1, 1, d) + 0.1 * torch.randn(B, Hq, T, d, generator=g)
+    rise = torch.linspace(0.0, 68.0 * d ** 0.5, S).view(1, 1, S, 1) / float(u @ u)
+    k = rise * u.view(1, 1, 1, d) + 0.05 * torch.randn(B, Hkv, S, d, generator=g)
+    v = torch.randn(B, Hkv, S, d, generator=g)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    out, lse = run_fwd_gpu(q, k, v, False, 0.0, 0)
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), causal=False)
+    say(f"rising logits: lse range {rl.min():.1f}..{rl.max():.1f} (nats)")
+    check_close(f64(out), ro, "bf16", "rising logits")
+    le = np.abs(f64(lse) - rl)
+    say(f"rising logits: lse max error {le.max():.3e}")
+    assert np.all(le <= 2e-2 + np.abs(rl) / 256)
