@@ -141,3 +141,29 @@ def test_decode_poisoned_tail_slots():
     out, lse = run_decode(d2, cfg["rope_base"])
     assert bool(torch.isfinite(out).all())
     assert torch.equal(out, clean) and torch.equal(lse, clean_lse)
+
+
+def test_decode_logits_rising_every_block():
+    """Cached keys whose logits grow along each sequence (a new maximum more than 2^8 above the
+    last in each of the first 8 blocks, then level near 40 nats), so the reference is raised in
+    every early block and again at the start of every piece of a split sequence."""
+    cfg, d = dec_inputs(num_seqs=4, Hq=8, Hkv=2, seq_lens=[40, 300, 700, 1500])
+    g = torch.Generator("cpu").manual_seed(9)
+    dh = cfg["d_h"]
+    u = torch.randn(dh, generator=g)
+    q = (u.view(1, 1, dh) + 0.1 * torch.randn(d["q"].shape, generator=g)).to(d["q"].dtype)
+    kc = d["k_cache"].float()
+    for b, L in enumerate(d["seq_lens"].tolist()):
+        for j in range(L):
+            phys = int(d["block_table"][b, j // 16])
+            # 8.5 (base 2) of logit per 16-token block for 8 blocks, then level (~47 nats)
+            kc[phys, :, j % 16] = min(j / 16.0, 8.0) * 8.5 * dh ** 0.5 / float(u @ u) * u / 1.4427 \
+                + 0.05 * torch.randn(dh, generator=g)
+    d = dict(d, q=q, k_cache=kc.to(d["k_cache"].dtype))
+    say("decode rising logits")
+    out, lse = run_decode(d, 0.0)
+    ro, rl = oracle_decode(d, 0.0)
+    check_close(f64(out), ro, "bf16", "decode rising logits")
+    le = np.abs(f64(lse) - rl)
+    say(f"decode rising logits: lse max error {le.max():.3e} (lse up to {rl.max():.1f})")
+    assert np.all(le <= 2e-2 + np.abs(rl) / 256)
