@@ -35,10 +35,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // 16 bytes from global memory straight into LDS (global_load_lds_dwordx4): lane i of the
 // wave writes lds_wave_base + 16 * i; lds_wave_base must be the same for the whole wave.
 // The builtin only exists for the device pass; keeping it out of the host pass keeps
-// clang emitting the host launch stubs of the kernels that use it.
+// clang emitting the host launch stubs of the kernels that use it.  kPolicy is the
+// instruction's cache-policy field: 0 (default) or kStreamPolicy.
+constexpr int kStreamPolicy = 2;  // "nt": data read once, streamed past the caches
+template <int kPolicy = 0>
 __device__ __forceinline__ void load_lds16(const void* gptr, void* lds_wave_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, kPolicy);
 #endif
 }
 
