@@ -24,6 +24,11 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libattn.so not built at {LIB_PATH}; run "
                           "`python -m exact_transformer_attention_amd.build` (or __graft_entry__.build())")
+    # PyTorch ships its own HIP runtime under the same soname as the system one.  Loading
+    # torch first makes libattn.so bind to that copy; loaded the other way round, the process
+    # holds two runtimes and the streams and device pointers torch hands over are not valid
+    # in the one libattn.so calls (its launches then fail).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i64, i32, vp]

@@ -201,3 +201,18 @@ def test_misaligned_pointers_rejected(lib):
     assert fwd(lib, out=odd) == e.ATTN_ERR_INVALID_ARG
     assert fwd(lib, lse=ctypes.c_void_p(0x1002)) == e.ATTN_ERR_INVALID_ARG
     assert fwd(lib, k=ctypes.c_void_p(0x1008)) == e.ATTN_ERR_INVALID_ARG
+
+
+def test_binding_shares_torchs_hip_runtime():
+    """The binding imported before torch must still leave one HIP runtime in the process:
+    torch bundles its own copy under the system runtime's soname, and a second copy would
+    not accept torch's streams or device pointers."""
+    import subprocess
+    import sys
+    code = ("import exact_transformer_attention_amd._lib, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().splitlines()[-1] == "1", r.stdout
