@@ -1,6 +1,8 @@
 """Prefill parity: libattn's attn_fwd (HIP, through the C ABI) against the fp64 oracle on
 the same seeded inputs."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -168,3 +170,31 @@ def test_bf16_logits_rising_every_block():
     le = np.abs(f64(lse) - rl)
     say(f"rising logits: lse max error {le.max():.3e}")
     assert np.all(le <= 2e-2 + np.abs(rl) / 256)
+
+
+@pytest.mark.gpu
+def test_binding_imported_before_torch_launches():
+    """A process that imports the binding before torch still runs the kernels on torch's
+    tensors and stream (the binding brings torch's HIP runtime in first)."""
+    import subprocess
+    import sys
+    code = "\n".join([
+        "import exact_transformer_attention_amd._lib as L",
+        "import numpy as np, torch, oracle, workloads",
+        "q, k, v = workloads.make_fwd_inputs(1, 4, 2, 80, 80, 128, dtype='bf16', seed=11)",
+        "dev = torch.device('cuda:0')",
+        "out, lse = L.attn_fwd(q.to(dev), k.to(dev), v.to(dev), causal=True, rope_base=10000.0)",
+        "torch.cuda.synchronize()",
+        "ref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(),",
+        "                       causal=True, rope_base=10000.0)",
+        "ref = ref[0] if isinstance(ref, tuple) else ref",
+        "print('maxabs', float(np.abs(out.float().cpu().double().numpy() - ref).max()), flush=True)",
+    ])
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    say("binding-before-torch subprocess: attn_fwd 1x4x2 T=S=80 d_h=128 causal bf16")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=240,
+                       env=dict(os.environ, PYTHONPATH=root + os.pathsep + os.path.join(root, "tests")))
+    assert r.returncode == 0, r.stderr[-3000:]
+    err = float(r.stdout.strip().splitlines()[-1].split()[1])
+    say(f"binding-before-torch: max abs error {err:.3e}")
+    assert err <= 2e-2
