@@ -341,30 +341,37 @@ def check_gqa_equals_repeated_mha(orc):
         assert not np.allclose(o3[:, first:], o[:, first:], atol=1e-6)
 
 
-def online_softmax_attention(qr, kr, v, mask, bounds):
-    """The blocked recurrence of the FlashAttention deep dive ("Why is attention O(n^2)..."):
-    running max m, normaliser l and unnormalised output o, rescaled by exp(m - m_new) per
-    key block; O = o / l at the end.  A row whose visible keys so far are none keeps m = -inf
-    (guarded so no NaN appears).  qr [T,d], kr [S,d], v [S,dv], mask [T,S] additive."""
+def blockwise_merge_attention(qr, kr, v, mask, bounds):
+    """Attention computed one key block at a time and then combined, as the FlashAttention
+    deep dive of "Why is attention O(n^2), how does FlashAttention help ..." argues is exact:
+    every block on its own gives a softmax-normalised output o_b over its keys and the log of
+    its normaliser, lse_b; since the full normaliser is the sum of the block normalisers,
+    lse = log sum_b exp(lse_b) and the full output is the average of the o_b weighted by
+    exp(lse_b - lse).  A block in which a row sees no key has lse_b = -inf and weight 0.
+    qr [T,d], kr [S,d], v [S,dv], mask [T,S] additive (0 or -inf); bounds: key blocks."""
     T, d = qr.shape
-    m = np.full(T, -np.inf)
-    ell = np.zeros(T)
-    o = np.zeros((T, v.shape[1]))
+    outs, lses = [], []
     for s0, s1 in bounds:
-        s = qr @ kr[s0:s1].T / math.sqrt(d) + mask[:, s0:s1]
-        m_new = np.maximum(m, s.max(axis=1))
-        m_use = np.where(np.isfinite(m_new), m_new, 0.0)
-        p = np.exp(s - m_use[:, None])
-        alpha = np.where(np.isfinite(m), np.exp(m - m_use), 0.0)
-        ell = alpha * ell + p.sum(axis=1)
-        o = alpha[:, None] * o + p @ v[s0:s1]
-        m = m_new
-    return o / ell[:, None], m + np.log(ell)
+        logits = qr @ kr[s0:s1].T / math.sqrt(d) + mask[:, s0:s1]
+        top = logits.max(axis=1)
+        live = np.isfinite(top)
+        shift = np.where(live, top, 0.0)
+        w = np.exp(logits - shift[:, None])              # 0 for hidden keys
+        z = np.where(live, w.sum(axis=1), 1.0)
+        outs.append(np.where(live[:, None], (w @ v[s0:s1]) / z[:, None], 0.0))
+        lses.append(np.where(live, shift + np.log(z), -np.inf))
+    lse_b = np.stack(lses)                               # [blocks, T]
+    top = lse_b.max(axis=0)
+    weight = np.exp(lse_b - top)                         # exp(-inf) = 0
+    total = weight.sum(axis=0)
+    out = np.einsum("bt,btd->td", weight, np.stack(outs)) / total[:, None]
+    return out, top + np.log(total)
 
 
 def check_online_recurrence_equals_full(orc):
-    """The recurrence over arbitrary key-block partitions (including blocks that are fully
-    masked for some rows) gives the full softmax result up to rounding."""
+    """Blocked evaluation over arbitrary key-block partitions (including blocks that are fully
+    masked for some rows), the blocks combined through their log-normalisers, gives the full
+    softmax result up to rounding."""
     rng = _rng(13)
     for trial in range(12):
         T = int(rng.integers(1, 40))
@@ -381,7 +388,7 @@ def check_online_recurrence_equals_full(orc):
         qr = orc.apply_rope(q[0, 0], pos + np.arange(T), base)
         kr = orc.apply_rope(k[0, 0], np.arange(S), base)
         mask = orc.causal_mask(pos + np.arange(T), np.arange(S))
-        o2, l2 = online_softmax_attention(qr, kr, v[0, 0], mask, bounds)
+        o2, l2 = blockwise_merge_attention(qr, kr, v[0, 0], mask, bounds)
         assert np.allclose(o2, o[0, 0], atol=1e-13), trial
         assert np.allclose(l2, l[0, 0], atol=1e-13), trial
 
@@ -699,7 +706,44 @@ def check_fp8_attention_scales(orc):
     assert np.allclose(o1, ro, atol=1e-12) and np.allclose(l1, rl, atol=1e-12)
 
 
+def check_error_metrics(orc):
+    """max_abs and rel_rms, the acceptance metrics of every parity test, against closed
+    forms: max_abs is the largest |got - ref| over the whole tensor (sign dropped, the
+    largest element, not a mean); rel_rms is ||got - ref||_2 / ||ref||_2 over the whole
+    tensor (one norm of everything, not per row); a NaN in got never passes a bound."""
+    ref = np.array([[1.0, -2.0, 3.0], [0.5, 0.0, -4.0]])
+    err = np.zeros_like(ref)
+    err[1, 2] = -0.37
+    assert orc.max_abs(ref + err, ref) == 0.37 or abs(orc.max_abs(ref + err, ref) - 0.37) < 1e-15
+    err[0, 1] = 0.125
+    assert abs(orc.max_abs(ref + err, ref) - 0.37) < 1e-15          # the largest, sign dropped
+    assert abs(orc.max_abs(ref - err, ref) - 0.37) < 1e-15
+    spread = np.array([0.1, 0.2, 0.5, -0.05])
+    assert abs(orc.max_abs(spread, np.zeros(4)) - 0.5) < 1e-15      # not the mean (0.2125)
+    assert orc.max_abs(np.zeros((0, 3)), np.zeros((0, 3))) == 0.0
+    assert orc.max_abs(ref, ref) == 0.0
+    rng = _rng(40)
+    r = rng.standard_normal((3, 5, 7))
+    for eps in (1e-3, -2.5e-2, 0.5):
+        assert abs(orc.rel_rms(r * (1.0 + eps), r) - abs(eps)) < 1e-14 * (1 + abs(eps))
+    # a 3-4-5 error against a 5-12-13 reference: 5 / 13
+    assert abs(orc.rel_rms(np.array([8.0, 16.0, 0.0]), np.array([5.0, 12.0, 0.0])) - 5.0 / 13.0) < 1e-15
+    # one norm over the whole tensor: rows of very different size
+    big = np.array([[1.0, 0.0], [0.0, 10.0]])
+    assert abs(orc.rel_rms(big + np.array([[1.0, 0.0], [0.0, 0.0]]), big) - 1.0 / math.sqrt(101.0)) < 1e-15
+    # independent of the tensor's size (no 1/N): the same relative error on 1 and on 4096 entries
+    one = np.array([2.0])
+    many = np.full(4096, 2.0)
+    assert abs(orc.rel_rms(one * 1.01, one) - orc.rel_rms(many * 1.01, many)) < 1e-15
+    assert orc.rel_rms(np.zeros(3), np.zeros(3)) == 0.0
+    bad = ref.copy()
+    bad[0, 0] = np.nan
+    assert not orc.max_abs(bad, ref) <= 1.0
+    assert not orc.rel_rms(bad, ref) <= 1.0
+
+
 ALL_CHECKS = [
+    check_error_metrics,
     check_fp8_decode, check_fp8_attention_scales,
     check_backward_finite_differences, check_backward_sampled_equals_full, check_backward_torch_autograd, check_backward_invariants,
     check_prefill_paged_equals_contiguous,

@@ -249,7 +249,52 @@ def m_fp8_v_not_transposed(mod):
               "v = fp8_e4m3_decode(vt8).reshape(vt8.shape[:-2] + (vt8.shape[-1], vt8.shape[-2])) * F64(v_scale)")
 
 
-MUTATIONS = [m_fp8_bias8, m_fp8_no_subnormals, m_fp8_v_not_transposed, m_bwd_missing_delta, m_bwd_rope_forward_not_transpose, m_bwd_gqa_overwrite,
+def m_rel_rms_no_sqrt(mod):
+    """rel-RMS as a ratio of squared norms."""
+    _resource(mod, "den = float(np.sqrt(np.sum(ref * ref)))\n    num = float(np.sqrt(np.sum((got - ref) ** 2)))",
+              "den = float(np.sum(ref * ref))\n    num = float(np.sum((got - ref) ** 2))")
+
+
+def m_rel_rms_num_no_sqrt(mod):
+    """The error's norm without its square root."""
+    _resource(mod, "num = float(np.sqrt(np.sum((got - ref) ** 2)))", "num = float(np.sum((got - ref) ** 2))")
+
+
+def m_rel_rms_per_element(mod):
+    """The ratio further divided by the element count."""
+    _resource(mod, "return num / den if den > 0 else num", "return num / den / got.size if den > 0 else num")
+
+
+def m_rel_rms_max_not_norm(mod):
+    """The largest error over the reference norm instead of the error norm."""
+    _resource(mod, "num = float(np.sqrt(np.sum((got - ref) ** 2)))", "num = float(np.max(np.abs(got - ref)))")
+
+
+def m_rel_rms_row_mean(mod):
+    """The mean of per-row relative errors instead of one norm over the tensor."""
+    _resource(mod, "return num / den if den > 0 else num",
+              "return float(np.mean(np.linalg.norm(np.atleast_2d(got - ref), axis=-1) / "
+              "np.maximum(np.linalg.norm(np.atleast_2d(ref), axis=-1), 1e-300))) if den > 0 else num")
+
+
+def m_max_abs_signed(mod):
+    """max_abs without the absolute value."""
+    _resource(mod, "np.max(np.abs(got - ref))", "np.max(got - ref)")
+
+
+def m_max_abs_mean(mod):
+    """The mean absolute error instead of the largest."""
+    _resource(mod, "np.max(np.abs(got - ref))", "np.mean(np.abs(got - ref))")
+
+
+def m_max_abs_ignores_nan(mod):
+    """NaN entries skipped, so a non-finite result could pass."""
+    _resource(mod, "np.max(np.abs(got - ref))", "np.nanmax(np.abs(got - ref))")
+
+
+MUTATIONS = [m_rel_rms_no_sqrt, m_rel_rms_num_no_sqrt, m_rel_rms_per_element, m_rel_rms_max_not_norm,
+             m_rel_rms_row_mean, m_max_abs_signed, m_max_abs_mean, m_max_abs_ignores_nan,
+             m_fp8_bias8, m_fp8_no_subnormals, m_fp8_v_not_transposed, m_bwd_missing_delta, m_bwd_rope_forward_not_transpose, m_bwd_gqa_overwrite,
              m_bwd_dk_unscaled, m_bwd_dk_uses_unrotated_q,
              m_window_off_by_one, m_mask_after_softmax, m_no_scale, m_scale_by_d, m_rope_freq_exponent, m_rope_clockwise,
              m_rope_rotate_half_pairs, m_rope_only_queries, m_gqa_modulo, m_causal_off_by_one,
