@@ -99,23 +99,61 @@ def _require(cond, msg):
         raise ValueError(msg)
 
 
-def _fwd_buffers(q, k, v, out, lse, want_lse):
+def _tensor(t, name, dim=None, shape=None, dtype=None):
+    """Structure of one tensor argument: dimensions, shape, dtype, contiguity."""
     import torch
-    _require(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D")
+    _require(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    if dim is not None:
+        _require(t.dim() == dim, f"{name} must be {dim}-D, got shape {tuple(t.shape)}")
+    if shape is not None:
+        _require(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None:
+        _require(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _on_device(named):
+    """Every tensor argument on one GPU (checked after the structure, before any C call)."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        _require(t.is_cuda, f"{name} must be a device (GPU) tensor")
+        dev = t.device if dev is None else dev
+        _require(t.device == dev, f"{name} is on {t.device}, other arguments on {dev}")
+
+
+def _fwd_buffers(q, k, v, out, lse, want_lse, check_device=True):
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _tensor(t, n, dim=4)
     B, Hq, T, d = q.shape
-    _require(k.shape[0] == B and v.shape == k.shape and k.shape[3] == d, "shape mismatch")
-    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
-    for t in (q, k, v):
-        _require(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
     Hkv, S = k.shape[1], k.shape[2]
+    _require(k.shape[0] == B and v.shape == k.shape and k.shape[3] == d, "q, k, v shapes do not match")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
-    _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "bad out")
+    _tensor(out, "out", shape=q.shape, dtype=q.dtype)
     if lse is not None:
-        _require(lse.shape == (B, Hq, T) and lse.dtype == torch.float32 and lse.is_contiguous(), "bad lse")
+        _tensor(lse, "lse", shape=(B, Hq, T), dtype=torch.float32)
+    if check_device:
+        _on_device((("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse)))
     return out, lse, (B, Hq, Hkv, T, S, d)
+
+
+def _paged_args(q, k_cache, v_cache, block_table, seq_lens, block_size, qdim):
+    import torch
+    _tensor(q, "q", dim=qdim)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _tensor(t, n, dim=4, dtype=q.dtype)
+    N, d = q.shape[0], q.shape[-1]
+    _require(k_cache.shape == v_cache.shape and k_cache.shape[2] == block_size and k_cache.shape[3] == d,
+             "caches must be [num_blocks, Hkv, block_size, d_h] like q")
+    _tensor(block_table, "block_table", dim=2, dtype=torch.int32)
+    _tensor(seq_lens, "seq_lens", shape=(N,), dtype=torch.int32)
+    _require(block_table.shape[0] == N, "block_table must have one row per sequence")
 
 
 def attn_fwd(q, k, v, causal=False, rope_base=0.0, pos=0, out=None, lse=None, want_lse=True,
@@ -146,17 +184,20 @@ def attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, causal=False, pos=0, ou
     vt8 [B,Hkv,d_h,S], uint8 (or float8_e4m3fn) device tensors of codes, value = code * scale.
     Returns (out bf16 [B,Hq,T,d_h], lse fp32 [B,Hq,T])."""
     import torch
-    for t in (q8, k8, vt8):
-        _require(t.dim() == 4 and t.element_size() == 1 and t.is_cuda and t.is_contiguous(),
-                 "q8, k8, vt8 must be contiguous 4-D one-byte device tensors")
+    for t, n in ((q8, "q8"), (k8, "k8"), (vt8, "vt8")):
+        _tensor(t, n, dim=4)
+        _require(t.element_size() == 1, f"{n} must hold one-byte codes")
     B, Hq, T, d = q8.shape
     Hkv, S = k8.shape[1], k8.shape[2]
-    _require(k8.shape == (B, Hkv, S, d) and vt8.shape == (B, Hkv, d, S), "shape mismatch")
+    _require(k8.shape == (B, Hkv, S, d) and vt8.shape == (B, Hkv, d, S), "q8, k8, vt8 shapes do not match")
     if out is None:
         out = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q8.device)
-    _require(out.shape == (B, Hq, T, d) and out.dtype == torch.bfloat16 and out.is_contiguous(), "bad out")
+    _tensor(out, "out", shape=(B, Hq, T, d), dtype=torch.bfloat16)
+    if lse is not None:
+        _tensor(lse, "lse", shape=(B, Hq, T), dtype=torch.float32)
+    _on_device((("q8", q8), ("k8", k8), ("vt8", vt8), ("out", out), ("lse", lse)))
     st = LIB.attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), _ptr(out), _ptr(lse), B, Hq, Hkv, T, S, d,
                           int(bool(causal)), float(q_scale), float(k_scale), float(v_scale), int(pos),
                           _stream(stream))
@@ -167,22 +208,21 @@ def attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, causal=False, pos=0, ou
 def attn_prefill_paged(q, k_cache, v_cache, block_table, seq_lens, block_size=16, rope_base=0.0, out=None,
                        lse=None, want_lse=True, stream=None):
     """Prefill of the last T tokens of each sequence over a paged cache.  q [N,Hq,T,d_h];
-    caches [num_blocks,Hkv,block_size,d_h]; block_table [N,max_blocks] int32; seq_lens [N]
-    int32 (all device tensors).  Returns (out [N,Hq,T,d_h], lse [N,Hq,T])."""
+    caches [num_blocks,Hkv,block_size,d_h] of q's dtype; block_table [N,max_blocks] int32;
+    seq_lens [N] int32 (all device tensors).  Returns (out [N,Hq,T,d_h], lse [N,Hq,T])."""
     import torch
-    _require(q.dim() == 4, "q must be [N, Hq, T, d_h]")
+    _paged_args(q, k_cache, v_cache, block_table, seq_lens, block_size, 4)
     N, Hq, T, d = q.shape
     num_blocks, Hkv = k_cache.shape[0], k_cache.shape[1]
-    _require(k_cache.shape == v_cache.shape and k_cache.shape[2] == block_size and k_cache.shape[3] == d,
-             "cache shape mismatch")
-    _require(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables must be int32")
-    _require(block_table.dim() == 2 and block_table.shape[0] == N and seq_lens.shape == (N,), "table shape")
-    for t in (q, k_cache, v_cache, block_table, seq_lens):
-        _require(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((N, Hq, T), dtype=torch.float32, device=q.device)
+    _tensor(out, "out", shape=q.shape, dtype=q.dtype)
+    if lse is not None:
+        _tensor(lse, "lse", shape=(N, Hq, T), dtype=torch.float32)
+    _on_device((("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table),
+                ("seq_lens", seq_lens), ("out", out), ("lse", lse)))
     st = LIB.attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
                                 block_size, N, Hq, Hkv, d, T, block_table.shape[1], num_blocks, float(rope_base),
                                 _ptr(out), _ptr(lse), _dtype_code(q), _stream(stream))
@@ -194,28 +234,36 @@ def attn_decode_workspace_bytes(num_seqs, Hq, Hkv, d_h, max_blocks_per_seq, bloc
     return int(LIB.attn_decode_workspace_bytes(num_seqs, Hq, Hkv, d_h, max_blocks_per_seq, block_size))
 
 
+def _workspace(ws, need, name="workspace"):
+    _tensor(ws, name, dim=1)
+    _require(ws.numel() * ws.element_size() >= need, f"{name} holds {ws.numel() * ws.element_size()} bytes, "
+                                                      f"{need} needed")
+
+
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, block_size=16, rope_base=0.0,
                       out=None, lse=None, workspace=None, want_lse=True, stream=None):
-    """One decode step over a paged cache.  q [N,Hq,d_h]; caches [num_blocks,Hkv,block_size,d_h];
-    block_table [N,max_blocks] int32; seq_lens [N] int32 (all device tensors).
+    """One decode step over a paged cache.  q [N,Hq,d_h]; caches [num_blocks,Hkv,block_size,d_h]
+    of q's dtype; block_table [N,max_blocks] int32; seq_lens [N] int32; workspace a 1-D device
+    buffer of at least attn_decode_workspace_bytes(...) bytes (all device tensors).
     Returns (out, lse)."""
     import torch
+    _paged_args(q, k_cache, v_cache, block_table, seq_lens, block_size, 3)
     N, Hq, d = q.shape
     num_blocks, Hkv = k_cache.shape[0], k_cache.shape[1]
-    _require(k_cache.shape == v_cache.shape and k_cache.shape[2] == block_size and k_cache.shape[3] == d,
-             "cache shape mismatch")
-    _require(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables must be int32")
-    _require(block_table.dim() == 2 and block_table.shape[0] == N and seq_lens.shape == (N,), "table shape")
-    for t in (q, k_cache, v_cache, block_table, seq_lens):
-        _require(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
     mbps = block_table.shape[1]
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    _tensor(out, "out", shape=q.shape, dtype=q.dtype)
+    if lse is not None:
+        _tensor(lse, "lse", shape=(N, Hq), dtype=torch.float32)
     need = attn_decode_workspace_bytes(N, Hq, Hkv, d, mbps, block_size)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _workspace(workspace, need)
+    _on_device((("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table),
+                ("seq_lens", seq_lens), ("out", out), ("lse", lse), ("workspace", workspace)))
     st = LIB.attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
                                block_size, N, Hq, Hkv, d, mbps, num_blocks, float(rope_base), _ptr(out),
                                _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -234,16 +282,20 @@ def attn_bwd(q, k, v, out, lse, dout, causal=False, window=0, rope_base=0.0, pos
     output gradient dout.  Same shapes and options as the forward call (window > 0 means the
     causal sliding window of attn_fwd_window).  Returns (dq, dk, dv)."""
     import torch
-    _, _, (B, Hq, Hkv, T, S, d) = _fwd_buffers(q, k, v, out, lse, True)
-    _require(dout.shape == q.shape and dout.dtype == q.dtype and dout.is_cuda and dout.is_contiguous(), "bad dout")
+    _require(out is not None and lse is not None, "the forward's out and lse are required")
+    _, _, (B, Hq, Hkv, T, S, d) = _fwd_buffers(q, k, v, out, lse, True, check_device=False)
+    _tensor(dout, "dout", shape=q.shape, dtype=q.dtype)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for t, ref in ((dq, q), (dk, k), (dv, v)):
-        _require(t.shape == ref.shape and t.dtype == ref.dtype and t.is_contiguous(), "bad gradient buffer")
+    for t, ref, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _tensor(t, n, shape=ref.shape, dtype=ref.dtype)
     need = attn_bwd_workspace_bytes(B, Hq, Hkv, T, S, d, rope_base)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _workspace(workspace, need)
+    _on_device((("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse), ("dout", dout), ("dq", dq), ("dk", dk),
+                ("dv", dv), ("workspace", workspace)))
     st = LIB.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                       B, Hq, Hkv, T, S, d, int(bool(causal)), int(window), float(rope_base), int(pos),
                       _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(q),
@@ -253,13 +305,21 @@ def attn_bwd(q, k, v, out, lse, dout, causal=False, window=0, rope_base=0.0, pos
 
 
 def attn_paged_gather(cache, block_table, seq_lens, block_size=16, dst=None, stream=None):
-    """Contiguous copy [N,Hkv,max_blocks*block_size,d_h] of each sequence's cached rows via
-    the decode kernels' block-table address code.  Rows past a sequence keep dst's contents."""
+    """Contiguous copy [N,Hkv,max_blocks*block_size,d_h] of each sequence's cached rows through
+    the decode kernel's own read path (table windows, addresses, staging).  cache
+    [num_blocks,Hkv,block_size,d_h] with 256-byte rows; block_table [N,max_blocks] int32;
+    seq_lens [N] int32; rows past a sequence keep dst's contents."""
     import torch
+    _tensor(cache, "cache", dim=4)
+    _tensor(block_table, "block_table", dim=2, dtype=torch.int32)
     num_blocks, Hkv, bs, d = cache.shape
     N, mbps = block_table.shape
+    _require(bs == block_size, "cache blocks must hold block_size tokens")
+    _tensor(seq_lens, "seq_lens", shape=(N,), dtype=torch.int32)
     if dst is None:
         dst = torch.zeros((N, Hkv, mbps * block_size, d), dtype=cache.dtype, device=cache.device)
+    _tensor(dst, "dst", shape=(N, Hkv, mbps * block_size, d), dtype=cache.dtype)
+    _on_device((("cache", cache), ("block_table", block_table), ("seq_lens", seq_lens), ("dst", dst)))
     st = LIB.attn_paged_gather(_ptr(cache), _ptr(block_table), _ptr(seq_lens), block_size, N, Hkv, d, mbps,
                                num_blocks, cache.element_size(), _ptr(dst), _stream(stream))
     _check(st, "attn_paged_gather")

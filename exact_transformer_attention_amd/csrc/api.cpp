@@ -59,6 +59,8 @@ attn_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, f
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
   if (d_h != 64 && d_h != 128) return ATTN_ERR_UNSUPPORTED;
   if (pos > ((int64_t)1 << 40) || pos < -((int64_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
+  // the bf16 kernel reads one KV head's keys through a 32-bit buffer range
+  if (dtype == ATTN_BF16 && (uint64_t)S * (uint64_t)d_h * 2u > 0xffffffffull) return ATTN_ERR_UNSUPPORTED;
 
   attn::FwdParams p;
   std::memset(&p, 0, sizeof(p));
@@ -314,14 +316,29 @@ attn_status_t attn_paged_gather(const void* cache, const int32_t* block_table, c
                                 int block_size, int num_seqs, int Hkv, int d_h, int max_blocks_per_seq,
                                 int num_blocks, int elem_bytes, void* dst, void* stream) {
   if (!cache || !block_table || !seq_lens || !dst) return ATTN_ERR_INVALID_ARG;
-  if (misaligned(cache, 4) || misaligned(dst, 4) || misaligned(block_table, 4) || misaligned(seq_lens, 4))
+  if (misaligned(cache, 16) || misaligned(dst, 16) || misaligned(block_table, 4) || misaligned(seq_lens, 4))
     return ATTN_ERR_INVALID_ARG;
   if (num_seqs < 1 || Hkv < 1 || d_h < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || block_size < 1)
     return ATTN_ERR_INVALID_ARG;
   if (elem_bytes != 2 && elem_bytes != 4) return ATTN_ERR_INVALID_ARG;
-  if (block_size != 16 || (d_h * elem_bytes) % 64 != 0) return ATTN_ERR_UNSUPPORTED;
-  hipError_t e = attn::launch_paged_gather(cache, block_table, seq_lens, num_seqs, Hkv, d_h,
-                                           max_blocks_per_seq, elem_bytes, dst, (hipStream_t)stream);
+  // the decode kernel's read path: 16-token blocks of 256-byte rows (bf16, d_h = 128)
+  if (block_size != 16 || d_h * elem_bytes != 256) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)num_seqs * Hkv * max_blocks_per_seq > (1LL << 30)) return ATTN_ERR_UNSUPPORTED;
+
+  attn::DecodeParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.k_cache = cache;
+  p.v_cache = cache;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.num_seqs = num_seqs;
+  p.Hq = Hkv;
+  p.Hkv = Hkv;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.nwaves = attn::decode_num_waves(num_seqs, Hkv, max_blocks_per_seq);
+  p.copy_dst = dst;
+  hipError_t e = attn::launch_paged_gather(p, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -49,16 +49,6 @@ __device__ __forceinline__ size_t slice_offset(int phys, int Hkv, int kvh, int d
   return (((size_t)phys * Hkv + kvh) * kDecBlock) * (size_t)d;
 }
 
-// Element offset of the (physical block, kv head) slice holding token block `j` of
-// sequence `b`.  Used by the gather kernel; the decode kernel reads the same entries
-// 64 at a time and forms the same offset.
-__device__ __forceinline__ size_t paged_slice(const int32_t* __restrict__ block_table,
-                                              int max_blocks_per_seq, int b, int j, int Hkv,
-                                              int kvh, int d) {
-  const int phys = block_table[(size_t)b * max_blocks_per_seq + j];
-  return slice_offset(phys, Hkv, kvh, d);
-}
-
 // 16-byte chunk position of chunk c of token row t inside a staged K block: reading
 // chunk c of all 16 rows (the MFMA operand pattern) then hits 16 distinct bank groups.
 __device__ __forceinline__ int kpos(int t, int c) { return t * 16 + (c ^ t); }
@@ -121,6 +111,10 @@ struct Piece {
   int b, kvh, j0, n, L, slot;
 };
 
+// COPY: the same read path (work division, table windows, address, LDS ring) with the
+// attention replaced by a copy of each staged K block to p.copy_dst, so that the block-table
+// translation the decode performs can be compared bit for bit with a plain gather.
+template <bool COPY>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) char ring[];  // kDecodeLds bytes
 
@@ -140,7 +134,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   __syncthreads();
 
   const SeqScan sc = scan_seqs(p.seq_lens, p.num_seqs, mbps, lane);
-  if (w == 0) {  // block offsets of every sequence, for the merge kernel
+  if (!COPY && w == 0) {  // block offsets of every sequence, for the merge kernel
     int acc = sc.excl;
     for (int i = 0; i < sc.q; ++i) {
       const int b = lane * sc.q + i;
@@ -189,7 +183,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       raw[kk] = (u32x4){0u, 0u, 0u, 0u};
-      if (l16 < G)
+      if (!COPY && l16 < G)
         raw[kk] = *(const u32x4*)((const __bf16*)p.q + ((size_t)pc.b * p.Hq + head) * kDecD + grp * 8 + 32 * kk);
     }
   };
@@ -310,6 +304,28 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     const int L = cp.L;
     const char* kst = ring + (gstep % kStages) * kStageBytes;
     const char* vst = kst + kStageBytes / 2;
+    if constexpr (COPY) {
+      // staged K: LDS chunk t * 16 + l16 holds chunk l16 ^ t of token t (issue, below kpos)
+      char* dst = (char*)p.copy_dst + ((size_t)cp.b * Hkv + cp.kvh) * (size_t)mbps * kDecBlock * (kDecD * 2);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * r + grp;
+        const int tok = j * kDecBlock + t;
+        const u32x4 v = *(const u32x4*)(kst + (t * 16 + l16) * 16);
+        if (tok < L) *(u32x4*)(dst + (size_t)tok * (kDecD * 2) + (l16 ^ t) * 16) = v;
+      }
+      ++gstep;
+      if (++ci < cp.n) {
+        if (np_state == 0 && cp.n - ci <= kLookahead) fetch_np();
+        continue;
+      }
+      if (np_state != 1) break;
+      cp = np;
+      np_state = 0;
+      ci = 0;
+      if (cp.n <= kLookahead) fetch_np();
+      continue;
+    }
 
     // S^T = K q^T for the 16 tokens of the block.
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -478,32 +494,6 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
   if (p.lse && d == 0) p.lse[bh] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
 }
 
-// Exact copy of each sequence's cached rows through the block table.
-__global__ __launch_bounds__(256) void paged_gather_kernel(const char* cache, const int32_t* block_table,
-                                                           const int32_t* seq_lens, int Hkv, int d_h,
-                                                           int max_blocks_per_seq, int elem_bytes,
-                                                           char* dst) {
-  int w = blockIdx.x;
-  const int j = w % max_blocks_per_seq;
-  w /= max_blocks_per_seq;
-  const int kvh = w % Hkv;
-  const int b = w / Hkv;
-  const int L = seq_lens[b];
-  const int nblk = (L + kDecBlock - 1) / kDecBlock;
-  if (j >= nblk) return;
-  const size_t src = paged_slice(block_table, max_blocks_per_seq, b, j, Hkv, kvh, d_h);
-  const size_t row_bytes = (size_t)d_h * elem_bytes;
-  const size_t cap = (size_t)max_blocks_per_seq * kDecBlock;
-  for (int t = threadIdx.x / 16; t < kDecBlock; t += blockDim.x / 16) {
-    const int tok = j * kDecBlock + t;
-    if (tok >= L) break;
-    const char* s = cache + (src + (size_t)t * d_h) * elem_bytes;
-    char* dd = dst + (((size_t)b * Hkv + kvh) * cap + tok) * row_bytes;
-    for (size_t o = (threadIdx.x % 16) * 4; o < row_bytes; o += 64)
-      *(uint32_t*)(dd + o) = *(const uint32_t*)(s + o);
-  }
-}
-
 int decode_num_waves(int num_seqs, int Hkv, int max_blocks_per_seq) {
   const long long work = (long long)num_seqs * Hkv * max_blocks_per_seq;
   return (int)(work < kDecodeWaves ? work : kDecodeWaves);
@@ -515,7 +505,7 @@ long long decode_num_slots(int num_seqs, int Hkv, int max_blocks_per_seq) {
 
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
   constexpr size_t lds = kDecodeLds;
-  hipLaunchKernelGGL(decode_partial_kernel, dim3((unsigned)p.nwaves), dim3(64), lds, stream, p);
+  hipLaunchKernelGGL(decode_partial_kernel<false>, dim3((unsigned)p.nwaves), dim3(64), lds, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long grid = (long long)p.num_seqs * p.Hq;
@@ -524,13 +514,8 @@ hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_paged_gather(const void* cache, const int32_t* block_table, const int32_t* seq_lens,
-                               int num_seqs, int Hkv, int d_h, int max_blocks_per_seq, int elem_bytes,
-                               void* dst, hipStream_t stream) {
-  const long long grid = (long long)num_seqs * Hkv * max_blocks_per_seq;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(paged_gather_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const char*)cache,
-                     block_table, seq_lens, Hkv, d_h, max_blocks_per_seq, elem_bytes, (char*)dst);
+hipError_t launch_paged_gather(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_partial_kernel<true>, dim3((unsigned)p.nwaves), dim3(64), kDecodeLds, stream, p);
   return hipGetLastError();
 }
 

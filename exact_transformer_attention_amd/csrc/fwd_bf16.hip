@@ -21,9 +21,10 @@
 //    apart.
 //  * The running max is subtracted inside the matrix product: one extra k-step pairs
 //    a constant 1 on the K side with -m on the Q side, so the accumulators already
-//    hold s - m and each probability is a single exp2.  m is kept bf16-exact for that
-//    purpose; it is only a reference point, so any value works as long as the same one
-//    scales o, l and the final lse.
+//    hold s - m and each probability is a single exp2.  m is kept to a 16-bit significand
+//    for that purpose (the sum of two bf16 pieces, so the k-step subtracts it exactly at
+//    any magnitude); it is only a reference point, so any value works as long as the same
+//    one scales o, l and the final lse.
 //  * The reference is not recomputed every block.  Probabilities are formed against the
 //    current reference; only when a row has no reference yet, or a half block's row sum
 //    exceeds 2^16 (the reference is stale by more than ~16 in log2 units), is the exact
@@ -52,6 +53,7 @@
 #include "attn_common.h"
 #include "fwd_params.h"
 #include "launchers.h"
+#include "prefill_common.h"
 
 namespace attn {
 
@@ -74,31 +76,9 @@ struct Cfg {
   static constexpr int RSTEP = kWave / CPR;         // rows between a thread's chunks
 };
 
-// xor swizzle of the 16-byte chunk index of V row r: the transpose reads of a half
-// wave (4 rows x 64 bytes) then touch 16 distinct bank groups.
-template <int D>
-__device__ __forceinline__ int vswz(int r) {
-  if constexpr (D == 128) return 4 * (r & 3);
-  else return 4 * ((r >> 1) & 1);
-}
-
-__device__ __forceinline__ void cmul(float& c, float& s, float sc, float ss) {
-  const float nc = c * sc - s * ss;
-  const float ns = c * ss + s * sc;
-  c = nc;
-  s = ns;
-}
-
-// Round up to a bf16-representable value (finite x).
-__device__ __forceinline__ float bf16_ceil(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  uint32_t r = u & 0xffff0000u;
-  const float t = __builtin_bit_cast(float, r);
-  if (t < x) r = (x > 0.f) ? r + 0x10000u : r - 0x10000u;
-  return __builtin_bit_cast(float, r);
-}
-
-__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+using prefill::cmul;
+using prefill::max3;
+using prefill::vswz;
 
 }  // namespace
 
@@ -192,8 +172,9 @@ void fwd_bf16_kernel(FwdParams p) {
   // wait for those blocks
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   if constexpr (ROPE) __syncthreads();
-  // Extra k-step: K side holds 1 in slot 0 of the g = 0 lanes, Q side holds -m there.
-  const bf16x8 ones_op = __builtin_bit_cast(bf16x8, (u32x4){g == 0 ? 0x3f80u : 0u, 0u, 0u, 0u});
+  // Extra k-step: K side holds 1 in slots 0 and 1 of the g = 0 lanes, Q side holds -m there
+  // as two bf16 pieces (m has a 16-bit significand, so the pair is exact).
+  const bf16x8 ones_op = __builtin_bit_cast(bf16x8, (u32x4){g == 0 ? 0x3f803f80u : 0u, 0u, 0u, 0u});
 
   // ---- this thread's share of the K/V block copies: chunk `slot` of rows row0 + j*RSTEP.
   const int slot = lane % C::CPR;
@@ -309,7 +290,7 @@ void fwd_bf16_kernel(FwdParams p) {
   float m_ref[kNB], l_run[kNB];
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
-    m_ref[nb] = -INFINITY;  // bf16-exact reference max (base 2)
+    m_ref[nb] = -INFINITY;  // reference max (base 2), a 16-bit-significand value
     l_run[nb] = 0.f;
   }
   f32x16 o[C::DB][kNB];
@@ -335,8 +316,8 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
         const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-        const bf16x8 bop = __builtin_bit_cast(
-            bf16x8, (u32x4){g == 0 ? (__builtin_bit_cast(uint32_t, -bias) >> 16) : 0u, 0u, 0u, 0u});
+        const bf16x8 bop =
+            __builtin_bit_cast(bf16x8, (u32x4){g == 0 ? prefill::split_bf16_pair(-bias) : 0u, 0u, 0u, 0u});
         f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -479,7 +460,7 @@ void fwd_bf16_kernel(FwdParams p) {
       // 32-key half at a time; O^T += V^T P^T for that half.  The exact block max is only
       // needed when a row has no reference yet or a half's row sum exceeds 2^16 (the
       // reference is stale by more than ~16): then the reference is raised to the max
-      // (bf16-exact), o and l are rescaled, and the half is recomputed.
+      // (rounded up to a 16-bit significand), o and l are rescaled, and the half is recomputed.
       bf16x8 pop[kNB][4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
@@ -500,7 +481,7 @@ void fwd_bf16_kernel(FwdParams p) {
             const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
             const float tabs = tmax + bias;
             const bool need = tabs > m_ref[nb] + 8.f;
-            const float m_new = need ? bf16_ceil(tabs) : m_ref[nb];
+            const float m_new = need ? prefill::ceil_sig16(tabs) : m_ref[nb];
             const float alpha = need ? fast_exp2(m_ref[nb] - m_new) : 1.f;  // 0 when m_ref was -inf
             const float delta = need ? m_new - bias : 0.f;
             l_run[nb] *= alpha;

@@ -27,6 +27,7 @@ struct DecodeParams {
   float* part_o;      // [slots, Hq / Hkv, d_h] fp32 unnormalised outputs
   float* part_ml;     // [slots, Hq / Hkv, 2] fp32 (reference max in base 2, normaliser)
   int32_t* seq_prefix;  // [num_seqs + 1] cache blocks before each sequence (written by the kernel)
+  void* copy_dst;       // copy mode (attn_paged_gather): [num_seqs, Hkv, max_blocks_per_seq * 16] rows of 256 B
   int num_seqs, Hq, Hkv, max_blocks_per_seq, num_blocks;
   int nwaves;         // grid of the partial kernel: one wave per workgroup
   int use_rope;
@@ -40,9 +41,9 @@ int decode_num_waves(int num_seqs, int Hkv, int max_blocks_per_seq);
 // Partial-result slots the decode kernels may write for these sizes.
 long long decode_num_slots(int num_seqs, int Hkv, int max_blocks_per_seq);
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
-hipError_t launch_paged_gather(const void* cache, const int32_t* block_table,
-                               const int32_t* seq_lens, int num_seqs, int Hkv, int d_h,
-                               int max_blocks_per_seq, int elem_bytes, void* dst,
-                               hipStream_t stream);
+// The decode kernel's read path in copy mode: every staged cache block is written out in
+// sequence order instead of being attended to (p.k_cache is the cache, p.copy_dst the
+// destination; 256-byte rows).
+hipError_t launch_paged_gather(const DecodeParams& p, hipStream_t stream);
 
 }  // namespace attn

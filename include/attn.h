@@ -16,10 +16,9 @@
  *            block_table [num_seqs, max_blocks_per_seq] int32;  seq_lens [num_seqs] int32;
  *            lse [num_seqs, Hq] fp32
  * out has the dtype of the inputs; accumulation and lse are fp32.
- * Alignment: tensors of head rows (q, k, v, out, their gradients, the caches and the
- * workspaces) start on 16-byte boundaries, lse, block tables and sequence lengths on
- * 4-byte ones (the gather's cache and destination on 4-byte ones); otherwise the call
- * returns ATTN_ERR_INVALID_ARG.
+ * Alignment: tensors of head rows (q, k, v, out, their gradients, the caches, the gather's
+ * destination and the workspaces) start on 16-byte boundaries, lse, block tables and
+ * sequence lengths on 4-byte ones; otherwise the call returns ATTN_ERR_INVALID_ARG.
  */
 #ifndef LIBATTN_ATTN_H
 #define LIBATTN_ATTN_H
@@ -70,7 +69,9 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
  *   dtype    ATTN_F32 or ATTN_BF16 (bf16 inputs use bf16 MFMA with fp32 accumulation)
  *
  * Supported: d_h in {64, 128}; any B, Hq, Hkv >= 1 with Hq % Hkv == 0; any
- * T, S >= 1 (ragged tails are masked).  The 1/sqrt(d_h) scale is fixed.
+ * T, S >= 1 (ragged tails are masked) with S * d_h * 2 < 2^32 for bf16 (one KV head's
+ * keys are addressed through a 32-bit buffer range; ATTN_ERR_UNSUPPORTED otherwise).
+ * The 1/sqrt(d_h) scale is fixed.
  */
 ATTN_API attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                        int B, int Hq, int Hkv, int T, int S, int d_h, int causal,
@@ -215,13 +216,18 @@ ATTN_API size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d
                                    int max_blocks_per_seq, int block_size);
 
 /*
- * attn_paged_gather -- copy each sequence's cached rows into a contiguous buffer using
- * the same block-table address code as attn_decode_paged (an exact copy; it exists so
- * that the address translation can be checked bit for bit).
+ * attn_paged_gather -- copy each sequence's cached rows into a contiguous buffer through the
+ * read path of attn_decode_paged itself: the same work division, block-table reads (64
+ * entries at a time, broadcast across the wave), slice addresses (table entries clamped into
+ * [0, num_blocks)) and LDS staging, with the attention replaced by a copy.  It exists so that
+ * the decode's block-table translation ("Self-Attention Complexity, FlashAttention,
+ * PagedAttention, and RoPE in Code", Part 3) can be checked bit for bit.
  *
- *   cache        [num_blocks, Hkv, block_size, d_h] elements of elem_bytes (2 or 4)
- *   dst          [num_seqs, Hkv, max_blocks_per_seq * block_size, d_h]; rows j >= seq_lens[b]
- *                are left untouched
+ *   cache        [num_blocks, Hkv, block_size, d_h] elements of elem_bytes (2 or 4), 16-byte aligned
+ *   dst          [num_seqs, Hkv, max_blocks_per_seq * block_size, d_h], 16-byte aligned; rows
+ *                j >= seq_lens[b] are left untouched
+ * Supported: block_size == 16 and d_h * elem_bytes == 256 (the decode cache's rows: bf16,
+ * d_h = 128), num_seqs * Hkv * max_blocks_per_seq <= 2^30 (ATTN_ERR_UNSUPPORTED otherwise).
  */
 ATTN_API attn_status_t attn_paged_gather(const void* cache, const int32_t* block_table,
                                 const int32_t* seq_lens, int block_size, int num_seqs, int Hkv,

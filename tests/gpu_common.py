@@ -45,21 +45,6 @@ def check_close(got, ref, dtype, what, lse_got=None, lse_ref=None):
     return ma, rr
 
 
-def sample_rows(B, Hq, T, n, seed):
-    """(b, h, t) rows to check at full size: the first and last rows of several heads plus
-    random rows."""
-    rng = np.random.default_rng(seed)
-    rows = set()
-    for b in range(B):
-        for h in (0, Hq - 1, Hq // 2):
-            for t in (0, 1, 2, 3, 63, 64, 127, 128, T // 2, T - 2, T - 1):
-                if 0 <= t < T:
-                    rows.add((b, h, t))
-    while len(rows) < n:
-        rows.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(T))))
-    return np.array(sorted(rows), dtype=np.int64)
-
-
 def run_fwd_gpu(q, k, v, causal, rope_base, pos):
     from exact_transformer_attention_amd import attn_fwd
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()

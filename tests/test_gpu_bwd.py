@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
 import workloads
 from gpu_common import f64, say
 
@@ -106,24 +107,44 @@ def test_bwd_window_covering_everything_equals_causal():
         assert torch.equal(x, y)
 
 
-def test_bwd_gqa8k_sampled():
+def test_bwd_gqa8k_every_work_item():
     """The bench workload (causal GQA, B=2, Hq=32, Hkv=8, T=S=8192, RoPE 1e4) in the bench's
-    launch configuration; one KV head's dk, dv at sampled keys and dq at sampled rows of its
-    query heads, computed entry by entry by the oracle."""
+    launch configuration.  For every (batch, KV head): dk and dv at one random key of every
+    128-key block (each a work item of the dK/dV kernel) and dq at one random row of every
+    64-row query block of a random query head of the group (each a work item of the dQ
+    kernel), computed entry by entry by the oracle; the 16 KV heads in worker processes."""
     cfg = workloads.CONFIGS["gqa8k"]
     q, k, v, do = workloads.make_bwd_inputs(**cfg)
     say("bwd gqa8k: GPU forward + backward")
     dq, dk, dv = run_fwd_bwd(q, k, v, do, True, 0, cfg["rope_base"], 0)
-    b, g = 1, 5
-    keys = [0, 1, 63, 64, 127, 128, 4095, 4096, 8000, 8190, 8191]
-    rows = [(h, t) for h in (20, 21, 22, 23) for t in (0, 1, 127, 128, 1000, 2047, 4097, 6000, 8191)]
-    say("bwd gqa8k: oracle sampled")
-    rq, rk, rv = oracle.attention_backward_sampled(f64(q), f64(k), f64(v), f64(do), b, g, keys, rows, True,
-                                                   cfg["rope_base"], 0)
-    gq = np.array([f64(dq[b, h, t]) for h, t in rows])
-    check_grad(gq, rq, "dq rows")
-    check_grad(f64(dk[b, g, keys]), rk, "dk keys")
-    check_grad(f64(dv[b, g, keys]), rv, "dv keys")
+    B, Hq, Hkv, T, S = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], cfg["S"]
+    G = Hq // Hkv
+    rng = np.random.default_rng(45)
+    qf, kf, vf, dof = (oracle_pool.f32(x) for x in (q, k, v, do))
+    tasks, picks = [], []
+    for b in range(B):
+        for g in range(Hkv):
+            keys = [kb * 128 + int(rng.integers(128)) for kb in range(S // 128)]
+            rows = [(g * G + int(rng.integers(G)), qb * 64 + int(rng.integers(64))) for qb in range(T // 64)]
+            # the group's slices only (batch 0, KV head 0 of the slice, query heads 0..G-1)
+            sl_q, sl_kv = (slice(b, b + 1), slice(g * G, (g + 1) * G)), (slice(b, b + 1), slice(g, g + 1))
+            tasks.append(("attention_backward_sampled",
+                          (qf[sl_q], kf[sl_kv], vf[sl_kv], dof[sl_q], 0, 0, keys, [(h - g * G, t) for h, t in rows]),
+                          dict(causal=True, rope_base=cfg["rope_base"], pos=0)))
+            picks.append((b, g, keys, rows))
+    say(f"bwd gqa8k: oracle on {len(tasks)} KV heads")
+    res = oracle_pool.run(tasks)
+    gq, rq, gk, rk, gv, rv = [], [], [], [], [], []
+    for (b, g, keys, rows), (q_ref, k_ref, v_ref) in zip(picks, res):
+        gq.append(np.array([f64(dq[b, h, t]) for h, t in rows]))
+        rq.append(q_ref)
+        gk.append(f64(dk[b, g, keys]))
+        rk.append(k_ref)
+        gv.append(f64(dv[b, g, keys]))
+        rv.append(v_ref)
+    check_grad(np.concatenate(gq), np.concatenate(rq), "dq work items")
+    check_grad(np.concatenate(gk), np.concatenate(rk), "dk work items")
+    check_grad(np.concatenate(gv), np.concatenate(rv), "dv work items")
 
 
 def test_bwd_gqa8k_every_entry_written():

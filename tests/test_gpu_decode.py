@@ -78,21 +78,33 @@ def test_decode_long_runs():
         check_close(f64(out[b:b + 1].cpu()), ro, "bf16", f"long runs seq {b}", f64(lse[b:b + 1].cpu()), rl)
 
 
-def test_gather_bit_exact():
-    """The block-table address code, copied out by attn_paged_gather, equals the oracle's
-    gather bit for bit (both dtypes)."""
+@pytest.mark.parametrize("case", ["short", "long"])
+def test_gather_bit_exact(case):
+    """attn_paged_gather runs the decode kernel's own read path (runs cut into pieces, table
+    entries read 64 at a time and broadcast, the next piece looked up ahead, clamped slice
+    addresses, LDS staging) and copies each staged block out instead of attending to it: the
+    result equals the oracle's gather bit for bit.  "short": sequences of 1-900 tokens (pieces
+    crossing sequence boundaries); "long": 16 sequences of 30000-33000 tokens, so each wave's
+    run spans ~125 blocks and the 64-entry table windows are refilled inside a piece."""
     from exact_transformer_attention_amd import attn_paged_gather
-    cfg, d = dec_inputs(num_seqs=9, len_lo=1, len_hi=900)
-    for cache in (d["k_cache"], d["v_cache"].float()):
-        got = attn_paged_gather(cache.cuda(), d["block_table"].cuda(), d["seq_lens"].cuda()).cpu()
-        torch.cuda.synchronize()
-        for b in range(cfg["num_seqs"]):
-            L = int(d["seq_lens"][b])
-            ref = oracle.gather_paged(cache.numpy() if cache.dtype == torch.float32 else
-                                      cache.view(torch.int16).numpy(), d["block_table"][b].numpy(), L, 16)
-            g = got[b, :, :L]
-            g = g.numpy() if g.dtype == torch.float32 else g.view(torch.int16).numpy()
-            assert np.array_equal(g.view(np.uint8), ref.view(np.uint8)), b
+    if case == "short":
+        cfg, d = dec_inputs(num_seqs=9, len_lo=1, len_hi=900)
+        cache = d["k_cache"].cuda()
+    else:
+        cfg = workloads.scaled(workloads.CONFIGS["decode64"], num_seqs=16, len_lo=30000, len_hi=33000, seed=13)
+        d = workloads.make_decode_inputs(**cfg, device="cuda")
+        cache = d["k_cache"]
+        total = int(sum((int(L) + 15) // 16 for L in d["seq_lens"].tolist())) * cfg["Hkv"]
+        say(f"gather long: {total} (sequence, KV head, block) triples, {total / 2048:.0f} per wave")
+        assert total // 2048 > 64
+    got = attn_paged_gather(cache, d["block_table"].cuda(), d["seq_lens"].cuda())
+    torch.cuda.synchronize()
+    pool = cache.cpu().view(torch.int16).numpy()
+    for b in range(cfg["num_seqs"]):
+        L = int(d["seq_lens"][b])
+        ref = oracle.gather_paged(pool, d["block_table"][b].numpy(), L, 16)
+        g = got[b, :, :L].cpu().view(torch.int16).numpy()
+        assert np.array_equal(g, ref), b
 
 
 def test_decode_one_hot_exact():

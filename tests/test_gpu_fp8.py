@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
 import workloads
 from gpu_common import f64, say
 
@@ -84,23 +85,25 @@ def test_fp8_scales_fold():
     assert torch.allclose(b[0].float(), 2 * a[0].float(), rtol=1e-2, atol=1e-3)
 
 
-def test_fp8_gqa8k_sampled():
+def test_fp8_gqa8k_every_work_item():
     """The 8192-token causal GQA shape (B=2, Hq=32, Hkv=8) in the benchmark's launch
-    configuration; sampled rows computed one by one by the oracle."""
+    configuration: one row of every work item (each batch, KV-head group and 64-row query
+    block, a random query head of the group) plus the first 64 rows of every head, each
+    evaluated by the oracle on the decoded fp8 values."""
     cfg = workloads.CONFIGS["gqa8k"]
     (q8, k8, vt8), sc = workloads.make_fp8_inputs(**cfg)
     say("fp8 gqa8k: GPU")
     out, lse = run_fp8(q8, k8, vt8, sc, True, 0)
-    rows = [(b, h, t) for b in (0, 1) for h in (0, 13, 31) for t in (0, 1, 63, 64, 4095, 8191)]
+    rows = oracle_pool.work_item_rows(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], seed=43, first_rows=64)
     q = oracle.fp8_e4m3_decode(q8.numpy()) * sc[0]
     k = oracle.fp8_e4m3_decode(k8.numpy()) * sc[1]
     v = np.swapaxes(oracle.fp8_e4m3_decode(vt8.numpy()), -1, -2) * sc[2]
-    say("fp8 gqa8k: oracle rows")
-    ro, rl = oracle.attention_rows(q, k, v, rows, causal=True)
-    got = np.array([f64(out[b, h, t]) for b, h, t in rows])
-    gl = np.array([float(lse[b, h, t]) for b, h, t in rows])
+    say(f"fp8 gqa8k: oracle on {len(rows)} rows")
+    ro, rl = oracle_pool.attention_rows_grouped(q, k, np.ascontiguousarray(v), rows, True, 0.0)
+    idx = (rows[:, 0], rows[:, 1], rows[:, 2])
+    got, gl = f64(out)[idx], f64(lse)[idx]
     ma, rr = np.abs(got - ro).max(), oracle.rel_rms(got, ro)
-    say(f"fp8 gqa8k rows: max_abs={ma:.3e} rel_rms={rr:.3e} lse={np.abs(gl - rl).max():.3e}")
+    say(f"fp8 gqa8k work items: max_abs={ma:.3e} rel_rms={rr:.3e} lse={np.abs(gl - rl).max():.3e}")
     assert ma <= MAX_REL * np.abs(ro).max() and rr <= REL_RMS and np.abs(gl - rl).max() <= LSE_ABS
 
 

@@ -8,8 +8,9 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
 import workloads
-from gpu_common import check_close, f64, gen, run_fwd_gpu, sample_rows, say
+from gpu_common import check_close, f64, gen, run_fwd_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -97,22 +98,36 @@ def test_bf16_deterministic():
 
 # ------------------------------------------------------- full workloads ----
 
-@pytest.mark.parametrize("name", ["mha2k", "gqa8k", "gqa32k"])
-def test_full_workload_sampled_rows(name):
-    """Each full-size workload in the launch configuration the benchmark times; the oracle
-    evaluates a sample of rows (first/last rows of several heads plus random rows)."""
+@pytest.mark.parametrize("name", ["mha2k", "gqa8k"])
+def test_full_workload_every_element(name):
+    """The causal MHA (B=4, 32 heads, T=S=2048) and GQA (B=2, 32/8 heads, T=S=8192) workloads
+    in the launch configuration the benchmark times, compared with the oracle over the whole
+    output and lse (every head evaluated by the oracle in a worker process)."""
     cfg = workloads.CONFIGS[name]
     say(f"workload {name}: {cfg}")
     q, k, v = gen(cfg)
     out, lse = run_fwd_gpu(q, k, v, cfg["causal"], cfg["rope_base"], cfg["pos"])
+    say(f"workload {name}: oracle on {oracle_pool.pool_size()} workers")
+    ro, rl = oracle_pool.attention_per_head(oracle_pool.f32(q), oracle_pool.f32(k), oracle_pool.f32(v),
+                                            cfg["causal"], cfg["rope_base"], cfg["pos"])
+    check_close(f64(out), ro, "bf16", f"{name} every element", f64(lse), rl)
+
+
+def test_gqa32k_every_work_item():
+    """The 32768-token GQA workload in the benchmark's launch configuration: one row of every
+    work item of the kernel (each batch, KV-head group and 64-row query block, a random query
+    head of the group) and the first 256 rows of every head, each evaluated by the oracle."""
+    cfg = workloads.CONFIGS["gqa32k"]
+    say(f"workload gqa32k: {cfg}")
+    q, k, v = gen(cfg)
+    out, lse = run_fwd_gpu(q, k, v, cfg["causal"], cfg["rope_base"], cfg["pos"])
     assert bool(torch.isfinite(out).all()), "non-finite output"
-    rows = sample_rows(cfg["B"], cfg["Hq"], cfg["T"], 160, seed=cfg["seed"])
-    ro, rl = oracle.attention_rows(f64(q), f64(k), f64(v), rows,
-                                   causal=cfg["causal"], rope_base=cfg["rope_base"], pos=cfg["pos"])
+    rows = oracle_pool.work_item_rows(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], seed=cfg["seed"], first_rows=256)
+    say(f"workload gqa32k: oracle on {len(rows)} rows")
+    ro, rl = oracle_pool.attention_rows_grouped(oracle_pool.f32(q), oracle_pool.f32(k), oracle_pool.f32(v), rows,
+                                                cfg["causal"], cfg["rope_base"], cfg["pos"])
     idx = (rows[:, 0], rows[:, 1], rows[:, 2])
-    got = f64(out)[idx]
-    got_lse = f64(lse)[idx]
-    check_close(got, ro, "bf16", f"{name} sampled rows", got_lse, rl)
+    check_close(f64(out)[idx], ro, "bf16", "gqa32k work items", f64(lse)[idx], rl)
 
 
 @pytest.mark.parametrize("name", ["mha2k", "gqa8k", "gqa32k"])
@@ -198,3 +213,33 @@ def test_binding_imported_before_torch_launches():
     err = float(r.stdout.strip().splitlines()[-1].split()[1])
     say(f"binding-before-torch: max abs error {err:.3e}")
     assert err <= 2e-2
+
+
+def test_bf16_large_common_logit_offset():
+    """Every logit sits near 2^15 in base-2 units (all q and k rows close to one large common
+    vector), with a spread of a few units between keys.  The softmax only sees the differences;
+    the running reference must be able to sit at 2^15 with a fine enough grain that the
+    probabilities do not underflow (a bf16 reference has a grain of 256 there, which would
+    leave every probability below 2^-128).  No RoPE, so the bf16 rounding of the scaled q is
+    one common factor (relative 2^-9) on every logit: the output keeps the bf16 bounds and lse
+    is held to 2^-8 of its size plus the usual 2e-2, as in the other large-logit tests."""
+    B, Hq, Hkv, T, S, d = 1, 4, 2, 160, 200, 128
+    g = torch.Generator("cpu").manual_seed(77)
+    c = 44.75  # exact in bf16; c^2 * d * log2(e) / sqrt(d) ~ 2^15
+    q = torch.full((B, Hq, T, d), c)
+    # each k element is c or c +- 0.25 (the bf16 grain there) with probability 2 %
+    step = (torch.rand(B, Hkv, S, d, generator=g) < 0.02).float() * 0.25
+    sign = torch.where(torch.rand(B, Hkv, S, d, generator=g) < 0.5, -1.0, 1.0)
+    k = c + step * sign
+    v = torch.randn(B, Hkv, S, d, generator=g)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    for causal in (False, True):
+        out, lse = run_fwd_gpu(q, k, v, causal, 0.0, 0)
+        ro, rl = oracle.attention(f64(q), f64(k), f64(v), causal=causal)
+        say(f"large offset causal={causal}: lse {rl.min():.1f}..{rl.max():.1f} nats "
+            f"({rl.max() / np.log(2):.0f} in base 2)")
+        assert np.isfinite(f64(lse)).all(), "lse not finite"
+        check_close(f64(out), ro, "bf16", f"large common offset causal={causal}")
+        le = np.abs(f64(lse) - rl)
+        say(f"large offset causal={causal}: lse max error {le.max():.3e}")
+        assert np.all(le <= 2e-2 + np.abs(rl) / 256)

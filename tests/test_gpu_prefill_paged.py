@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
 import workloads
 from gpu_common import check_close, f64, say
 
@@ -67,15 +68,57 @@ def test_one_new_token_matches_decode():
     check_close(f64(out[:, :, 0]), f64(od), "bf16", "prefill T=1 vs decode", f64(lse[:, :, 0]), f64(ld))
 
 
-def test_prefill_paged_workload_sampled():
+def test_prefill_paged_workload_every_element():
     """The benchmark's shared-prefix workload (8 sequences, 6144-token shared prefix, 1024 new
-    tokens each) in the benchmark's launch configuration; two sequences and four heads
-    checked against the oracle."""
+    tokens each) in the benchmark's launch configuration, compared with the oracle over the
+    whole output and lse (one sequence per worker process)."""
     cfg = workloads.CONFIGS["prefix8"]
     d = workloads.make_prefill_paged_inputs(**cfg)
     out, lse = run(d, cfg["rope_base"])
     assert bool(torch.isfinite(out).all())
-    heads = [0, 9, 22, 31]
-    for b in (0, 7):
-        ro, rl = oracle_of(d, cfg["rope_base"], seqs=[b], heads=heads)
-        check_close(f64(out[b:b + 1, heads]), ro, "bf16", f"prefix8 seq {b}", f64(lse[b:b + 1, heads]), rl)
+    qf, kc, vc = (oracle_pool.f32(d[n]) for n in ("q", "k_cache", "v_cache"))
+    bt, sl = d["block_table"].numpy(), d["seq_lens"].numpy()
+    tasks = [("prefill_paged", (qf[b:b + 1], kc, vc, bt[b:b + 1], sl[b:b + 1], 16), dict(rope_base=cfg["rope_base"]))
+             for b in range(cfg["num_seqs"])]
+    say(f"prefix8: oracle on {len(tasks)} sequences")
+    res = oracle_pool.run(tasks)
+    ro = np.concatenate([r[0] for r in res])
+    rl = np.concatenate([r[1] for r in res])
+    check_close(f64(out), ro, "bf16", "prefix8 every element", f64(lse), rl)
+
+
+def test_prefill_paged_one_hot_exact():
+    """Block-table translation of the paged prefill, bit for bit.  In every (sequence, KV head)
+    each cached key is u = (1, ..., 1) except one token j, whose key is 0, and every query is
+    -16 u (no RoPE): the scaled logits are exactly 0 for token j and about -260 (base 2) for
+    every other key, whose exp2 underflows to exactly 0 in fp32, and the reference max settles
+    at exactly 0.  P is then one-hot with p_j = 1 and every output row of the group must equal
+    V_j bit for bit (lse exactly 0), wherever the table puts j's block.  Sequences of 1500 to
+    2100 tokens (94 to 132 table entries) over a randomly permuted pool."""
+    from exact_transformer_attention_amd import attn_prefill_paged
+    N, Hq, Hkv, T, d = 3, 8, 2, 48, 128
+    cfg = workloads.scaled(workloads.CONFIGS["decode64"], num_seqs=N, Hq=Hq, Hkv=Hkv, seq_lens=[1500, 2100, 1777],
+                           seed=71)
+    dd = workloads.make_decode_inputs(**cfg)
+    kc = torch.ones_like(dd["k_cache"])
+    vc = dd["v_cache"]
+    table = dd["block_table"]
+    rng = np.random.default_rng(71)
+    want = {}
+    for b in range(N):
+        L = int(dd["seq_lens"][b])
+        for g in range(Hkv):
+            j = int(rng.integers(0, L - T + 1))  # visible to every new row (rows sit at L - T + t)
+            phys, slot = int(table[b, j // 16]), j % 16
+            kc[phys, g, slot] = 0
+            want[(b, g)] = vc[phys, g, slot].clone()
+    q = torch.full((N, Hq, T, d), -16.0, dtype=torch.bfloat16)
+    say(f"paged prefill one-hot: lens {dd['seq_lens'].tolist()}, table width {table.shape[1]}")
+    out, lse = attn_prefill_paged(q.cuda(), kc.cuda(), vc.cuda(), table.cuda(), dd["seq_lens"].cuda(),
+                                  block_size=16, rope_base=0.0)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    for (b, g), v in want.items():
+        rows = out[b, g * (Hq // Hkv):(g + 1) * (Hq // Hkv)]  # [G, T, d]
+        assert torch.equal(rows.view(torch.int16), v.view(1, 1, d).expand_as(rows).view(torch.int16)), (b, g)
+    assert torch.all(lse == 0), float(lse.abs().max())

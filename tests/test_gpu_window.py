@@ -6,8 +6,9 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
 import workloads
-from gpu_common import check_close, f64, gen, sample_rows, say
+from gpu_common import check_close, f64, gen, say
 
 pytestmark = pytest.mark.gpu
 
@@ -59,16 +60,19 @@ def test_window_covering_everything_equals_causal():
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), w
 
 
-def test_window_full_workload_sampled_rows():
+def test_window_full_workload_every_work_item():
     """The 8192-token GQA workload with a 4096-key window, in the benchmark's launch
-    configuration; sampled rows against the oracle."""
+    configuration: one row of every work item (each batch, KV-head group and 64-row query
+    block, a random query head of the group) plus the first 128 rows of every head, each
+    evaluated by the oracle."""
     cfg = workloads.CONFIGS["gqa8k"]
     w = 4096
     q, k, v = gen(cfg)
     out, lse = run_window(q, k, v, w, cfg["rope_base"], cfg["pos"])
     assert bool(torch.isfinite(out).all())
-    rows = sample_rows(cfg["B"], cfg["Hq"], cfg["T"], 120, seed=41)
-    ro, rl = oracle.attention_rows(f64(q), f64(k), f64(v), rows, causal=True, rope_base=cfg["rope_base"],
-                                   pos=cfg["pos"], window=w)
+    rows = oracle_pool.work_item_rows(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], seed=41, first_rows=128)
+    say(f"window 4096: oracle on {len(rows)} rows")
+    ro, rl = oracle_pool.attention_rows_grouped(oracle_pool.f32(q), oracle_pool.f32(k), oracle_pool.f32(v), rows,
+                                                True, cfg["rope_base"], cfg["pos"], window=w)
     idx = (rows[:, 0], rows[:, 1], rows[:, 2])
-    check_close(f64(out)[idx], ro, "bf16", "gqa8k window 4096", f64(lse)[idx], rl)
+    check_close(f64(out)[idx], ro, "bf16", "gqa8k window 4096 work items", f64(lse)[idx], rl)
