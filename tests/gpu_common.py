@@ -7,11 +7,7 @@ import torch
 
 import oracle
 import workloads
-
-# Tolerances: fp32 max-abs 1e-5; bf16 max-abs 2e-2 and relative RMS 1e-2, against the
-# oracle evaluated on the same (bf16- or fp32-rounded) inputs.
-TOL = {"f32": dict(max_abs=1e-5, rel_rms=1e-5, lse=1e-5),
-       "bf16": dict(max_abs=2e-2, rel_rms=1e-2, lse=2e-2)}
+from tolerances import TOL  # against the oracle evaluated on the same (bf16- or fp32-rounded) inputs
 
 
 def say(*a):

@@ -9,31 +9,14 @@ import torch
 
 import oracle
 import workloads
+from cases import RANDOM_BWD_CASES, RANDOM_FP8_CASES, RANDOM_FWD_CASES, random_fp8_case
 from gpu_common import check_close, f64, say
+from tolerances import FP8
 
 pytestmark = pytest.mark.gpu
 
 
-def draw_fwd_cases(n, seed):
-    rng = np.random.default_rng(seed)
-    cases = []
-    for i in range(n):
-        Hkv = int(rng.choice([1, 2, 3]))
-        G = int(rng.choice([1, 2, 3, 4, 8]))
-        T = int(rng.integers(1, 260))
-        S = T + int(rng.choice([0, 0, int(rng.integers(1, 200))]))
-        mode = str(rng.choice(["causal", "full", "window"]))
-        window = int(rng.integers(1, S + 40)) if mode == "window" else 0
-        cases.append(dict(B=int(rng.integers(1, 3)), Hq=Hkv * G, Hkv=Hkv, T=T, S=S,
-                          d_h=int(rng.choice([64, 128])), mode=mode, window=window,
-                          rope_base=float(rng.choice([0.0, 10000.0, 500000.0])), pos=S - T, seed=1000 + i))
-    return cases
-
-
-FWD_CASES = draw_fwd_cases(24, seed=20260101)
-
-
-@pytest.mark.parametrize("c", FWD_CASES, ids=lambda c: f"{c['mode']}-{c['B']}x{c['Hq']}/{c['Hkv']}-"
+@pytest.mark.parametrize("c", RANDOM_FWD_CASES, ids=lambda c: f"{c['mode']}-{c['B']}x{c['Hq']}/{c['Hkv']}-"
                          f"{c['T']}x{c['S']}-d{c['d_h']}-w{c['window']}")
 def test_random_forward(c):
     from exact_transformer_attention_amd import attn_fwd, attn_fwd_window
@@ -51,10 +34,7 @@ def test_random_forward(c):
     check_close(f64(out), ro, "bf16", "out", f64(lse), rl)
 
 
-BWD_CASES = [c for c in draw_fwd_cases(40, seed=20260202) if c["d_h"] == 128][:8]
-
-
-@pytest.mark.parametrize("c", BWD_CASES, ids=lambda c: f"{c['mode']}-{c['B']}x{c['Hq']}/{c['Hkv']}-"
+@pytest.mark.parametrize("c", RANDOM_BWD_CASES, ids=lambda c: f"{c['mode']}-{c['B']}x{c['Hq']}/{c['Hkv']}-"
                          f"{c['T']}x{c['S']}-w{c['window']}")
 def test_random_backward(c):
     from exact_transformer_attention_amd import attn_bwd, attn_fwd, attn_fwd_window
@@ -106,26 +86,23 @@ def test_random_decode(c):
     check_close(f64(out), ro, "bf16", "decode", f64(lse), rl)
 
 
-@pytest.mark.parametrize("c", [c for c in draw_fwd_cases(40, seed=20260404) if c["mode"] != "window"][:8],
+@pytest.mark.parametrize("c", RANDOM_FP8_CASES,
                          ids=lambda c: f"{c['mode']}-{c['B']}x{c['Hq']}/{c['Hkv']}-{c['T']}x{c['S']}")
 def test_random_fp8(c):
     from exact_transformer_attention_amd import attn_fwd_fp8
-    S = (c["S"] + 3) // 4 * 4  # the fp8 path takes S in multiples of 4
-    T = min(c["T"], S)
-    causal = c["mode"] == "causal"
+    T, S, causal, pos = random_fp8_case(c)
     say(f"random fp8 {c} (T={T}, S={S})")
     (q8, k8, vt8), sc = workloads.make_fp8_inputs(B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], T=T, S=S, d_h=128,
                                                   seed=c["seed"])
-    out, lse = attn_fwd_fp8(q8.cuda(), k8.cuda(), vt8.cuda(), *sc, causal=causal, pos=S - T)
+    out, lse = attn_fwd_fp8(q8.cuda(), k8.cuda(), vt8.cuda(), *sc, causal=causal, pos=pos)
     torch.cuda.synchronize()
-    ro, rl = oracle.attention_fp8(q8.numpy(), k8.numpy(), vt8.numpy(), *sc, causal=causal, pos=S - T)
-    from test_gpu_fp8 import LSE_ABS, MAX_REL, REL_RMS
+    ro, rl = oracle.attention_fp8(q8.numpy(), k8.numpy(), vt8.numpy(), *sc, causal=causal, pos=pos)
     got, gl = f64(out), f64(lse)
     ma, rr = np.abs(got - ro).max(), oracle.rel_rms(got, ro)
     fin = np.isfinite(rl)
     le = np.abs(gl[fin] - rl[fin]).max() if fin.any() else 0.0
     say(f"fp8: max_abs={ma:.3e} rel_rms={rr:.3e} lse={le:.3e}")
-    assert ma <= MAX_REL * np.abs(ro).max() and rr <= REL_RMS and le <= LSE_ABS
+    assert ma <= FP8["max_rel"] * max(np.abs(ro).max(), 1e-2) and rr <= FP8["rel_rms"] and le <= FP8["lse"]
 
 
 def draw_paged_cases(n, seed):
