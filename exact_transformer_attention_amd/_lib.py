@@ -12,7 +12,9 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libattn.so")
 
-ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP, ATTN_ERR_SCRATCH = range(6)
+# bytes of device scratch attn_decode_paged_static holds per GPU (ATTN_DECODE_STATIC_SCRATCH_BYTES)
+DECODE_STATIC_SCRATCH_BYTES = 32 << 20
 ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTED = ("attn_fwd", "attn_fwd_window", "attn_fwd_fp8", "attn_prefill_paged", "attn_decode_paged",
@@ -41,6 +43,9 @@ def _load():
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp,
                                       vp, sz, i32, vp]
     lib.attn_decode_paged.restype = i32
+    lib.attn_decode_paged_static.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp,
+                                             i32, vp]
+    lib.attn_decode_paged_static.restype = i32
     lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_paged_gather.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
@@ -269,6 +274,34 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, block_size=16,
                                _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _dtype_code(q), _stream(stream))
     _check(st, "attn_decode_paged")
+    return out, lse
+
+
+def attn_decode_paged_static(q, k_cache, v_cache, block_table, seq_lens, block_size=16, rope_base=0.0,
+                             out=None, lse=None, want_lse=True, stream=None):
+    """attn_decode_paged without a workspace: the C entry point keeps the partial results in the
+    library's static per-GPU scratch and allocates nothing (pass out, and lse or
+    want_lse=False, for a call that allocates nothing here either).  Requests whose workspace
+    would exceed DECODE_STATIC_SCRATCH_BYTES fail (RuntimeError).  Calls overlapping in time on
+    one GPU share the scratch and race.  Returns (out, lse)."""
+    import torch
+    _paged_args(q, k_cache, v_cache, block_table, seq_lens, block_size, 3)
+    N, Hq, d = q.shape
+    num_blocks, Hkv = k_cache.shape[0], k_cache.shape[1]
+    mbps = block_table.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    _tensor(out, "out", shape=q.shape, dtype=q.dtype)
+    if lse is not None:
+        _tensor(lse, "lse", shape=(N, Hq), dtype=torch.float32)
+    _on_device((("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table),
+                ("seq_lens", seq_lens), ("out", out), ("lse", lse)))
+    st = LIB.attn_decode_paged_static(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                      block_size, N, Hq, Hkv, d, mbps, num_blocks, float(rope_base), _ptr(out),
+                                      _ptr(lse), _dtype_code(q), _stream(stream))
+    _check(st, "attn_decode_paged_static")
     return out, lse
 
 

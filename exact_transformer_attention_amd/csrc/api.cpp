@@ -38,6 +38,7 @@ const char* attn_status_str(attn_status_t s) {
     case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP runtime error";
+    case ATTN_ERR_SCRATCH: return "request larger than the static decode scratch";
   }
   return "unknown status";
 }
@@ -265,11 +266,16 @@ size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_h, int m
   return parts * ((size_t)d_h + 2) * sizeof(float) + ((size_t)num_seqs + 1) * sizeof(int32_t);
 }
 
-attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                                const int32_t* block_table, const int32_t* seq_lens, int block_size,
-                                int num_seqs, int Hq, int Hkv, int d_h, int max_blocks_per_seq,
-                                int num_blocks, float rope_base, void* out, float* lse, void* workspace,
-                                size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of a decode request (everything but the workspace); on success *need holds the
+// workspace bytes the request takes.
+attn_status_t decode_check(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                           const int32_t* seq_lens, int block_size, int num_seqs, int Hq, int Hkv, int d_h,
+                           int max_blocks_per_seq, int num_blocks, float rope_base, const void* out,
+                           const float* lse, attn_dtype_t dtype, size_t* need) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return ATTN_ERR_INVALID_ARG;
   if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(out, 16) ||
       misaligned(lse, 4) || misaligned(block_table, 4) || misaligned(seq_lens, 4))
@@ -283,10 +289,14 @@ attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* 
   if (dtype != ATTN_BF16 || d_h != 128 || block_size != 16 || Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
   if ((long long)num_seqs * Hkv * max_blocks_per_seq > (1LL << 30) || (long long)num_seqs * Hq > (1LL << 30))
     return ATTN_ERR_UNSUPPORTED;
-  const size_t need = attn_decode_workspace_bytes(num_seqs, Hq, Hkv, d_h, max_blocks_per_seq, block_size);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (misaligned(workspace, 16)) return ATTN_ERR_INVALID_ARG;
+  *need = attn_decode_workspace_bytes(num_seqs, Hq, Hkv, d_h, max_blocks_per_seq, block_size);
+  return ATTN_OK;
+}
 
+attn_status_t decode_launch(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                            const int32_t* seq_lens, int num_seqs, int Hq, int Hkv, int d_h, int max_blocks_per_seq,
+                            int num_blocks, float rope_base, void* out, float* lse, void* workspace,
+                            hipStream_t stream) {
   attn::DecodeParams p;
   std::memset(&p, 0, sizeof(p));
   p.q = q;
@@ -308,8 +318,43 @@ attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* 
   p.seq_prefix = (int32_t*)(p.part_ml + nparts * 2);
   p.use_rope = rope_base > 0.f;
   fill_rope(p.rope_c, d_h, p.use_rope ? rope_base : 1.f);
-  hipError_t e = attn::launch_decode_paged(p, (hipStream_t)stream);
+  hipError_t e = attn::launch_decode_paged(p, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                                int num_seqs, int Hq, int Hkv, int d_h, int max_blocks_per_seq,
+                                int num_blocks, float rope_base, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
+  size_t need = 0;
+  const attn_status_t st = decode_check(q, k_cache, v_cache, block_table, seq_lens, block_size, num_seqs, Hq, Hkv,
+                                        d_h, max_blocks_per_seq, num_blocks, rope_base, out, lse, dtype, &need);
+  if (st != ATTN_OK) return st;
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (misaligned(workspace, 16)) return ATTN_ERR_INVALID_ARG;
+  return decode_launch(q, k_cache, v_cache, block_table, seq_lens, num_seqs, Hq, Hkv, d_h, max_blocks_per_seq,
+                       num_blocks, rope_base, out, lse, workspace, (hipStream_t)stream);
+}
+
+attn_status_t attn_decode_paged_static(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                                       int num_seqs, int Hq, int Hkv, int d_h, int max_blocks_per_seq,
+                                       int num_blocks, float rope_base, void* out, float* lse, attn_dtype_t dtype,
+                                       void* stream) {
+  size_t need = 0;
+  const attn_status_t st = decode_check(q, k_cache, v_cache, block_table, seq_lens, block_size, num_seqs, Hq, Hkv,
+                                        d_h, max_blocks_per_seq, num_blocks, rope_base, out, lse, dtype, &need);
+  if (st != ATTN_OK) return st;
+  if (need > ATTN_DECODE_STATIC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (attn::decode_static_scratch((hipStream_t)stream, &scratch) != hipSuccess) return ATTN_ERR_HIP;
+  return decode_launch(q, k_cache, v_cache, block_table, seq_lens, num_seqs, Hq, Hkv, d_h, max_blocks_per_seq,
+                       num_blocks, rope_base, out, lse, scratch, (hipStream_t)stream);
 }
 
 attn_status_t attn_paged_gather(const void* cache, const int32_t* block_table, const int32_t* seq_lens,

@@ -32,6 +32,9 @@
 // common path has no cross-lane reduction.
 #include <math.h>
 
+#include <mutex>
+
+#include "attn.h"
 #include "attn_common.h"
 #include "launchers.h"
 
@@ -517,6 +520,43 @@ hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
 hipError_t launch_paged_gather(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(decode_partial_kernel<true>, dim3((unsigned)p.nwaves), dim3(64), kDecodeLds, stream, p);
   return hipGetLastError();
+}
+
+// Workspace of attn_decode_paged_static, for callers that cannot allocate: the same partial
+// results attn_decode_paged keeps in the caller's workspace.  Each GPU holds its own copy for
+// the life of the process.  In host code `scratch` only names the symbol (the host-side
+// stand-in is not a device address); the device address comes from hipGetSymbolAddress, taken
+// once per GPU with that GPU current, and is the only form passed to kernels.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_static_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    if (!addr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = addr;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace attn

@@ -38,6 +38,9 @@ struct DecodeParams {
 // (ten 16 KiB LDS rings per compute unit).
 constexpr int kDecodeWaves = 2048;
 int decode_num_waves(int num_seqs, int Hkv, int max_blocks_per_seq);
+// Device address of the decode's static scratch on the GPU that `stream` belongs to (the
+// current GPU for the null stream); looked up once per GPU.
+hipError_t decode_static_scratch(hipStream_t stream, void** ptr);
 // Partial-result slots the decode kernels may write for these sizes.
 long long decode_num_slots(int num_seqs, int Hkv, int max_blocks_per_seq);
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);

@@ -37,7 +37,8 @@ typedef enum {
   ATTN_ERR_INVALID_ARG = 1,  /* NULL pointer, non-positive size, Hq % Hkv != 0, bad table size */
   ATTN_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (d_h, dtype, block_size) */
   ATTN_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than the *_workspace_bytes() size */
-  ATTN_ERR_HIP = 4           /* the HIP runtime rejected a launch */
+  ATTN_ERR_HIP = 4,          /* the HIP runtime rejected a launch */
+  ATTN_ERR_SCRATCH = 5       /* request larger than the static scratch of attn_decode_paged_static */
 } attn_status_t;
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
@@ -149,6 +150,32 @@ ATTN_API attn_status_t attn_decode_paged(const void* q, const void* k_cache, con
                                 int max_blocks_per_seq, int num_blocks, float rope_base,
                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
                                 attn_dtype_t dtype, void* stream);
+
+/* Bytes of device scratch attn_decode_paged_static holds per GPU (32 MiB). */
+#define ATTN_DECODE_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * attn_decode_paged_static -- attn_decode_paged with no workspace argument that allocates
+ * nothing, for callers that cannot allocate device memory: code under HIP graph capture,
+ * serving loops that must not enter an allocator, harnesses that forbid allocation.
+ *
+ * The partial results that attn_decode_paged keeps in the caller's workspace live instead in
+ * a device array of ATTN_DECODE_STATIC_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends; its address is looked up (hipGetSymbolAddress) on the first call
+ * on each GPU.  A request for which attn_decode_workspace_bytes(...) exceeds that size
+ * returns ATTN_ERR_SCRATCH before anything is launched (e.g. with Hq / Hkv = 4 it fits up to
+ * num_seqs * Hkv = 14000; with Hq / Hkv = 16 up to 1900).  Arguments, checks, errors and
+ * results are otherwise those of attn_decode_paged, and the outputs are bit-identical to it.
+ * All calls on one GPU share that GPU's array, which keeps the last call's contents (the
+ * kernels need it in no particular state): calls that overlap in time on one GPU, from two
+ * streams or two host threads, race, and the caller must order them.  The call makes no
+ * hipMalloc, hipFree or other allocating request.
+ */
+ATTN_API attn_status_t attn_decode_paged_static(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int block_size, int num_seqs, int Hq, int Hkv, int d_h,
+                                int max_blocks_per_seq, int num_blocks, float rope_base,
+                                void* out, float* lse, attn_dtype_t dtype, void* stream);
 
 /*
  * attn_prefill_paged -- prefill (or chunked prefill) of T new query tokens per sequence

@@ -25,8 +25,8 @@ def lib():
 def test_header_declares_entry_points():
     names = header_functions()
     assert names == sorted(["attn_fwd", "attn_fwd_window", "attn_fwd_fp8", "attn_prefill_paged", "attn_decode_paged",
-                            "attn_decode_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes",
-                            "attn_paged_gather", "attn_status_str"])
+                            "attn_decode_paged_static", "attn_decode_workspace_bytes", "attn_bwd",
+                            "attn_bwd_workspace_bytes", "attn_paged_gather", "attn_status_str"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -43,8 +43,8 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     import exact_transformer_attention_amd as e
     assert e.attn_status_str(e.ATTN_OK) == "ok"
-    for s in range(1, 5):
-        assert e.attn_status_str(s) != "ok"
+    for s in range(1, 6):
+        assert e.attn_status_str(s) not in ("ok", "unknown status")
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
@@ -104,6 +104,41 @@ def dec(lib, **kw):
 ])
 def test_decode_validation(lib, kw, status):
     assert dec(lib, **kw) == status
+
+
+def dec_static(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, bs=16, N=4, Hq=32, Hkv=8, d=128, mbps=10, nb=40,
+             base=10000.0, out=FAKE, lse=None, dtype=1)
+    a.update(kw)
+    return lib.attn_decode_paged_static(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["bs"], a["N"], a["Hq"],
+                                        a["Hkv"], a["d"], a["mbps"], a["nb"], a["base"], a["out"], a["lse"],
+                                        a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(kc=None), 1), (dict(bt=None), 1), (dict(sl=None), 1), (dict(out=None), 1),
+    (dict(N=0), 1), (dict(Hq=30), 1), (dict(mbps=0), 1), (dict(nb=0), 1), (dict(bs=0), 1),
+    (dict(base=-2.0), 1), (dict(dtype=5), 1),
+    (dict(dtype=0), 2), (dict(d=64), 2), (dict(bs=32), 2), (dict(Hq=64, Hkv=2), 2),
+    (dict(N=1 << 20, mbps=1 << 12), 2),
+    # requests whose workspace passes the static scratch: rejected before any HIP call
+    (dict(N=4000), 5), (dict(N=300, Hq=128), 5),
+])
+def test_decode_static_validation(lib, kw, status):
+    assert dec_static(lib, **kw) == status
+
+
+def test_decode_static_scratch_limit(lib):
+    """The header's scratch size, the binding's copy of it, and the limits the header quotes:
+    with Hq / Hkv = 4 up to num_seqs * Hkv = 14000 fits, with Hq / Hkv = 16 up to 1900."""
+    import exact_transformer_attention_amd as e
+    m = re.search(r"#define ATTN_DECODE_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    limit = int(m.group(1)) << int(m.group(2))
+    assert limit == e.DECODE_STATIC_SCRATCH_BYTES
+    for G, fits in ((4, 14000), (16, 1900)):
+        # num_seqs * Hkv = fits with Hkv = 8, long sequences (the most partial-result slots)
+        assert 0 < lib.attn_decode_workspace_bytes(fits // 8, 8 * G, 8, 128, 4096, 16) <= limit
+    assert lib.attn_decode_workspace_bytes(2000, 32, 8, 128, 4096, 16) > limit
 
 
 def prefill_paged(lib, **kw):

@@ -75,6 +75,17 @@ def test_decode_rejections(L):
     raises(lambda: L.attn_decode_paged(q, kc, vc, bt, sl), "device")
 
 
+def test_decode_static_rejections(L):
+    q, kc, vc, bt, sl = paged()
+    raises(lambda: L.attn_decode_paged_static(q[None], kc, vc, bt, sl), "q must be 3-D")
+    raises(lambda: L.attn_decode_paged_static(q, kc, vc.float(), bt, sl), "v_cache must be")
+    raises(lambda: L.attn_decode_paged_static(q, kc, vc, bt, sl.long()), "seq_lens must be")
+    raises(lambda: L.attn_decode_paged_static(q, kc, vc, bt, sl, out=torch.zeros(2, 4, 64, dtype=bf16)),
+           "out must have shape")
+    raises(lambda: L.attn_decode_paged_static(q, kc, vc, bt, sl, lse=torch.zeros(2, 4, dtype=bf16)), "lse must be")
+    raises(lambda: L.attn_decode_paged_static(q, kc, vc, bt, sl), "device")
+
+
 def test_prefill_paged_rejections(L):
     q, kc, vc, bt, sl = paged(T=5)
     raises(lambda: L.attn_prefill_paged(q[0], kc, vc, bt, sl), "q must be 4-D")
