@@ -36,6 +36,7 @@ def kernel_sources_digest(files):
 
 
 PREFILL_SOURCES = ["exact_transformer_attention_amd/csrc/fwd_bf16.hip",
+                   "exact_transformer_attention_amd/csrc/prefill_common.h",
                    "exact_transformer_attention_amd/csrc/attn_common.h",
                    "exact_transformer_attention_amd/csrc/fwd_params.h"]
 DECODE_SOURCES = ["exact_transformer_attention_amd/csrc/decode.hip",
