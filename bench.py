@@ -244,6 +244,92 @@ def window_bench(a):
     print(json.dumps(res), flush=True)
 
 
+def cpu_baseline_config(name, cfg):
+    """The fp64 oracle on a bounded sample of a contiguous prefill workload: the whole of the
+    2048-token MHA shape; for the 32768-token shape the last 2048 rows of the query heads of
+    KV head 0 of batch 0 (each row against every key it sees)."""
+    import numpy as np
+    import oracle
+    import workloads
+    q, k, v = workloads.make_fwd_inputs(**cfg)
+    if name == "mha2k":
+        qs, ks, vs, t0, heads = q, k, v, 0, cfg["B"] * cfg["Hq"]
+        sample = f"the whole workload ({cfg['B']} x {cfg['Hq']} heads, all {cfg['T']} rows)"
+    else:
+        G = cfg["Hq"] // cfg["Hkv"]
+        t0 = cfg["T"] - 2048
+        qs, ks, vs = q[:1, :G, t0:], k[:1, :1], v[:1, :1]
+        heads = G
+        sample = f"batch 0, query heads 0-{G - 1} (KV head 0), rows {t0}-{cfg['T'] - 1} against every visible key"
+    qs, ks, vs = (x.double().numpy() for x in (qs, ks, vs))
+    t_start = time.perf_counter()
+    oracle.attention(qs, ks, vs, causal=True, rope_base=cfg["rope_base"], pos=t0, row_block=1024)
+    dt = time.perf_counter() - t_start
+    rows = np.arange(t0, cfg["T"])
+    flops = float(heads) * float(np.sum(rows + 1)) * cfg["d_h"] * 4.0  # exact visible pairs, 4 d_h each
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cpu_threads(), kind="oracle", seconds=round(dt, 3),
+                sample=f"{sample}, fp64 numpy, 1024-row blocks; {flops:.3e} FLOP (exact visible pairs)")
+
+
+def config_bench(a, name):
+    """Causal prefill of one of the other contiguous workloads (the 2048-token MHA shape or the
+    32768-token GQA shape), timed like the headline prefill (one JSON line)."""
+    import torch
+    import workloads
+    from exact_transformer_attention_amd import attn_fwd
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS[name]
+    q, k, v = (t.to(dev) for t in workloads.make_fwd_inputs(**cfg))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def run():
+        attn_fwd(q, k, v, causal=True, rope_base=cfg["rope_base"], pos=cfg["pos"], out=out, lse=lse)
+
+    steps, warmup = a.steps, a.warmup
+    if name == "gqa32k":  # each launch is ~8 ms: fewer launches keep the run short
+        steps, warmup = max(3, a.steps // 4), max(2, a.warmup // 8)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    avg = sum(ms) / len(ms)
+    assert bool(torch.isfinite(out).all())
+    if a.copy_calibration:
+        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+    flops = workloads.fwd_flops(**cfg)
+    tf = flops / (avg * 1e-3) / 1e12
+    G = cfg["Hq"] // cfg["Hkv"]
+    hp = 4 if G % 4 == 0 else (2 if G % 2 == 0 else 1)
+    res = {
+        "metric": "attention fwd TFLOP/s + % bf16 MFMA peak",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(avg, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded iid normal, bf16-rounded)",
+        "config": {"workload": f"causal prefill {name}: B={cfg['B']} Hq={cfg['Hq']} Hkv={cfg['Hkv']} "
+                               f"T=S={cfg['T']} d_h={cfg['d_h']} RoPE {cfg['rope_base']:g} sigma {cfg['sigma']:g}",
+                   **{k_: cfg[k_] for k_ in ("B", "Hq", "Hkv", "T", "S", "d_h", "causal", "rope_base")}},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(name, kernel_sources_digest(PREFILL_SOURCES)),
+                     "kernel": f"fwd_bf16_kernel<128,{hp}>", "flop_per_launch": flops, "avg_launch_ms": round(avg, 4)},
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_config(name, cfg)
+    print(json.dumps(res), flush=True)
+
+
 def prefix_bench(a):
     """Paged prefill of 1024 new tokens per sequence, 8 sequences over one shared 6144-token
     prefix (one JSON line)."""
@@ -467,7 +553,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "decode", "window", "prefix", "bwd", "fp8"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "window", "prefix", "bwd", "fp8", "mha2k", "gqa32k"],
+                    default=None,
                     help="time only one part (profiling runs); 'window' times the causal sliding-window "
                          "prefill (attn_fwd_window) on the same 8192-token GQA workload instead; 'prefix' "
                          "the paged prefill (attn_prefill_paged) of 8 sequences over a shared 6144-token prefix; "
@@ -480,7 +567,8 @@ def main():
     a = ap.parse_args()
     if a.traffic_from:
         print(json.dumps(summarize_pmc(a.traffic_from[0], a.traffic_from[1], os.path.join(ROOT, "profiles"),
-                                       extra_kind=a.only if a.only in ("window", "prefix", "bwd", "fp8") else None),
+                                       extra_kind=a.only if a.only in ("window", "prefix", "bwd", "fp8", "mha2k", "gqa32k")
+                                       else None),
                          indent=1))
         return
     if a.gpus != 1:
@@ -499,6 +587,9 @@ def main():
         return
     if a.only == "fp8":
         fp8_bench(a)
+        return
+    if a.only in ("mha2k", "gqa32k"):
+        config_bench(a, a.only)
         return
 
     import torch
