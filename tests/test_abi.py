@@ -64,6 +64,8 @@ def fwd(lib, **kw):
     (dict(Hq=6, Hkv=4), 1), (dict(causal=2), 1), (dict(base=-1.0), 1), (dict(base=float("nan")), 1),
     (dict(base=float("inf")), 1), (dict(dtype=7), 1),
     (dict(d=96), 2), (dict(d=256), 2), (dict(pos=1 << 41), 2),
+    # one KV head's bf16 keys past a 32-bit byte range (S * d_h * 2 >= 2^32)
+    (dict(S=1 << 24), 2), (dict(S=1 << 25, d=64), 2),
 ])
 def test_fwd_validation(lib, kw, status):
     assert fwd(lib, **kw) == status
