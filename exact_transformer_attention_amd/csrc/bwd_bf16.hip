@@ -619,11 +619,21 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(s[r]);
       if (need_mask) {
+        // element r holds key k0 + mb*32 + g*4 + c, c = (r/4)*8 + r%4: visible iff
+        // lo <= c <= hi, this query's first and last visible keys relative to
+        // k0 + mb*32 + g*4, clamped to 32 bits (opaque to the compiler, which would otherwise
+        // compare every element against the 64-bit bounds)
+        const int64_t base = (int64_t)k0 + mb * 32 + g * 4;
+        int64_t hi = (int64_t)S - 1 - base;
+        if (p.causal && lim - base < hi) hi = lim - base;
+        const int64_t lo = p.window > 0 ? lim - p.window + 1 - base : 0;
+        int hi32 = (int)(hi < -1 ? -1 : (hi > 32 ? 32 : hi));
+        int lo32 = (int)(lo < 0 ? 0 : (lo > 32 ? 32 : lo));
+        asm volatile("" : "+v"(hi32), "+v"(lo32));
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kk = k0 + mb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-          const bool ok = kk < S && (!p.causal || (int64_t)kk <= lim) && (p.window <= 0 || (int64_t)kk > lim - p.window);
-          if (!ok) pr[r] = 0.f;
+          const int c = (r / 4) * 8 + (r % 4);
+          pr[r] = ((c <= hi32) & (c >= lo32)) ? pr[r] : 0.f;
         }
       }
 #pragma unroll

@@ -442,17 +442,29 @@ void fwd_bf16_kernel(FwdParams p) {
       const bool need_mask = (k0 + kBN > S) || (p.causal && (int64_t)(k0 + kBN - 1) > pos + wrow0) ||
                              (p.window > 0 && (int64_t)k0 < lo_wave + kQW - 1);
       if (need_mask) {
+        // Element (mb, r) of this lane holds key k0 + g*4 + c with the compile-time offset
+        // c = mb*32 + (r/4)*8 + r%4; it is visible iff lo <= c <= hi, the bounds being this
+        // query's first and last visible keys relative to k0 + g*4, clamped to 32 bits.
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
           const int64_t lim = pos + wrow0 + nb * 32 + l32;  // last visible key of this query
+          const int64_t base = (int64_t)k0 + g * 4;
+          int64_t hi = (int64_t)S - 1 - base;
+          if (p.causal && lim - base < hi) hi = lim - base;
+          int64_t lo = 0;
+          if (p.window > 0) lo = lim - p.window + 1 - base;
+          int hi32 = (int)(hi < -1 ? -1 : (hi > kBN ? kBN : hi));
+          int lo32 = (int)(lo < 0 ? 0 : (lo > kBN ? kBN : lo));
+          // opaque to the compiler, which would otherwise compare every element against the
+          // 64-bit bounds
+          asm volatile("" : "+v"(hi32), "+v"(lo32));
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int key = k0 + mb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-              const bool vis = key < S && (!p.causal || (int64_t)key <= lim) &&
-                               (p.window <= 0 || (int64_t)key > lim - p.window);
-              if (!vis) s[mb][nb][r] = -INFINITY;
+              const int c = mb * 32 + (r / 4) * 8 + (r % 4);
+              const bool vis = (c <= hi32) & (c >= lo32);
+              s[mb][nb][r] = vis ? s[mb][nb][r] : -INFINITY;
             }
         }
       }

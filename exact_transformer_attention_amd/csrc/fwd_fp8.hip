@@ -198,14 +198,21 @@ void fwd_fp8_kernel(FwdParams p) {
     // the exponent below
     const bool need_mask = (k0 + kBlk > S) || (p.causal && (int64_t)(k0 + kBlk - 1) > pos + wrow0);
     if (need_mask) {
+      // element (mb, r) holds key k0 + g*4 + c, c = mb*32 + (r/4)*8 + r%4: visible iff
+      // c <= hi, this query's last visible key relative to k0 + g*4, clamped to 32 bits
+      // (opaque to the compiler, which would otherwise compare against the 64-bit bound)
       const int64_t lim = pos + t;
+      const int64_t base = (int64_t)k0 + g * 4;
+      int64_t hi = (int64_t)S - 1 - base;
+      if (p.causal && lim - base < hi) hi = lim - base;
+      int hi32 = (int)(hi < -1 ? -1 : (hi > kBlk ? kBlk : hi));
+      asm volatile("" : "+v"(hi32));
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + mb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-          const bool vis = key < S && (!p.causal || (int64_t)key <= lim);
-          s[mb][r] = vis ? s[mb][r] : -INFINITY;
+          const int c = mb * 32 + (r / 4) * 8 + (r % 4);
+          s[mb][r] = (c <= hi32) ? s[mb][r] : -INFINITY;
         }
     }
     // probabilities against the current reference; if a row has none yet or a half-block sum
