@@ -489,7 +489,7 @@ void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) u32x4 Vs0[kTileChunks], Vs1[kTileChunks];
 
   const int tid = threadIdx.x;
-  const int wid = tid / kWave;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: scalar values and branches
   const int lane = tid % kWave;
   const int l32 = lane % 32;
   const int g = lane / 32;

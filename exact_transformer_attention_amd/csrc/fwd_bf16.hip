@@ -96,7 +96,7 @@ void fwd_bf16_kernel(FwdParams p) {
   __shared__ int32_t tbl[PAGED ? kMaxPagedBlocks : 1];                     // block table row
 
   const int tid = threadIdx.x;
-  const int wid = tid / kWave;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: scalar values and branches
   const int lane = tid % kWave;
   const int l32 = lane % 32;
   const int g = lane / 32;

@@ -80,7 +80,7 @@ void fwd_fp8_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t Vt0[kDim * kBlk / 4], Vt1[kDim * kBlk / 4];
 
   const int tid = threadIdx.x;
-  const int wid = tid / kWave;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: scalar values and branches
   const int lane = tid % kWave;
   const int l32 = lane % 32;
   const int g = lane / 32;
