@@ -288,10 +288,19 @@ void fwd_bf16_kernel(FwdParams p) {
 
   // ---- running state: two query n-blocks per lane.
   float m_ref[kNB], l_run[kNB];
+  // Q side of the extra k-step: -m as two bf16 pieces in slots 0 and 1 of the g = 0 lanes
+  // (0 while a row has no reference yet).  Rebuilt only when the reference is raised.
+  bf16x8 bop[kNB];
+  auto set_bias = [&](int nb) {
+    const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
+    const uint32_t w = prefill::split_bf16_pair(-bias);
+    bop[nb] = __builtin_bit_cast(bf16x8, (u32x4){g == 0 ? w : 0u, 0u, 0u, 0u});
+  };
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     m_ref[nb] = -INFINITY;  // reference max (base 2), a 16-bit-significand value
     l_run[nb] = 0.f;
+    set_bias(nb);
   }
   f32x16 o[C::DB][kNB];
 #pragma unroll
@@ -315,13 +324,10 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
-        const float bias = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-        const bf16x8 bop =
-            __builtin_bit_cast(bf16x8, (u32x4){g == 0 ? prefill::split_bf16_pair(-bias) : 0u, 0u, 0u, 0u});
         f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-        s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_op, bop, acc, 0, 0, 0);
+        s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_op, bop[nb], acc, 0, 0, 0);
       }
     u32x4 out[C::NCH];
     float c[4], sn[4];
@@ -367,7 +373,7 @@ void fwd_bf16_kernel(FwdParams p) {
   auto expo = [&](f32x16 (&s)[2][kNB], int mb, bf16x8 (&pop)[kNB][4], float (&lt)[kNB]) {
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-      float lsum = 0.f;
+      float lsum;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         u32x4 pk;
@@ -376,7 +382,7 @@ void fwd_bf16_kernel(FwdParams p) {
           const float p0 = fast_exp2(s[mb][nb][8 * h + 2 * e]);
           const float p1 = fast_exp2(s[mb][nb][8 * h + 2 * e + 1]);
           pk[e] = pack_bf16(p0, p1);
-          lsum += p0 + p1;
+          lsum = (h == 0 && e == 0) ? p0 + p1 : lsum + (p0 + p1);
         }
         pop[nb][mb * 2 + h] = __builtin_bit_cast(bf16x8, pk);
       }
@@ -502,6 +508,7 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
               for (int r = 0; r < 16; ++r) o[db][nb][r] *= alpha;
             m_ref[nb] = m_new;
+            set_bias(nb);
             // this half and the next one were computed against the old reference
 #pragma unroll
             for (int mm = mb; mm < 2; ++mm)
