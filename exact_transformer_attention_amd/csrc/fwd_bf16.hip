@@ -153,25 +153,26 @@ void fwd_bf16_kernel(FwdParams p) {
   // Only the raw rows are loaded here (with the RoPE frequencies, staged in LDS); the
   // rotation and scaling run in the prologue below, while the first K/V blocks are in
   // flight.
+  // The frequency is requested first, so that its wait leaves the Q rows in flight; rows
+  // past T load row T - 1 instead (finite values whose outputs are never stored; no
+  // per-row branch between the requests).
+  __shared__ double ropec_s[ROPE ? D / 2 : 1];
+  double rope_c = 0.0;
+  if constexpr (ROPE) {
+    if (tid < D / 2) rope_c = p.rope_c[tid];
+  }
   bf16x8 qop[kNB][C::KS];
   u32x4 qraw[kNB][C::KS];
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
-    const int t = wrow0 + nb * 32 + l32;
+    const int t = min(wrow0 + nb * 32 + l32, T - 1);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      qraw[nb][ks] = (u32x4){0u, 0u, 0u, 0u};
-      if (t < T) qraw[nb][ks] = *(const u32x4*)(qg + (size_t)t * D + ks * 16 + g * 8);
-    }
+    for (int ks = 0; ks < C::KS; ++ks) qraw[nb][ks] = *(const u32x4*)(qg + (size_t)t * D + ks * 16 + g * 8);
   }
-  __shared__ double ropec_s[ROPE ? D / 2 : 1];
   if constexpr (ROPE) {
-    if (tid < D / 2) ropec_s[tid] = p.rope_c[tid];
+    if (tid < D / 2) ropec_s[tid] = rope_c;
+    __syncthreads();
   }
-  // Q rows landed before the K/V blocks are requested: a later wait for them would also
-  // wait for those blocks
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  if constexpr (ROPE) __syncthreads();
   // Extra k-step: K side holds 1 in slots 0 and 1 of the g = 0 lanes, Q side holds -m there
   // as two bf16 pieces (m has a 16-bit significand, so the pair is exact).
   const bf16x8 ones_op = __builtin_bit_cast(bf16x8, (u32x4){g == 0 ? 0x3f803f80u : 0u, 0u, 0u, 0u});
@@ -529,8 +530,29 @@ void fwd_bf16_kernel(FwdParams p) {
     wait_loads();  // this thread's loads issued above have landed before the next barrier
   };
 
-  // ---- prologue: raw K of the first two blocks and V of the first in flight; the first
-  // rotated.  The first block is 0, or the first one a sliding window reaches.
+  // ---- prologue.  RoPE angles of Q: the HP = 4 heads of a workgroup share their 64
+  // positions, so the (sin, cos) table of those positions is computed once, eight entries
+  // per thread, into LDS (rows padded to D/2 + 2 entries), and each lane reads its 32.
+  // This runs while the Q rows are in flight.
+  constexpr bool kQTab = ROPE && HP == 4 && RH == 64;
+  constexpr int kTabStride = D / 2 + 2;  // float2 entries per table row
+  __shared__ __attribute__((aligned(16))) float2 qtab[kQTab ? RH * kTabStride : 1];
+  if constexpr (kQTab) {
+    const int64_t p0 = pos + (int64_t)qb * RH;
+#pragma unroll
+    for (int k = 0; k < RH * (D / 2) / kThreads; ++k) {
+      const int e = tid + k * kThreads, r = e / (D / 2), i = e % (D / 2);
+      float sn, cs;
+      sincos_rev(rope_turns(p0 + r, ropec_s[i]), &sn, &cs);
+      qtab[r * kTabStride + i] = make_float2(sn, cs);
+    }
+    // before the block copies: a barrier with direct-to-LDS loads in flight waits for them
+    __syncthreads();
+  }
+  // Raw K of the first two blocks and V of the first in flight; the first rotated.  The
+  // first block is 0, or the first one a sliding window reaches.  They are requested
+  // before the Q rows are waited for, so the two latencies overlap (loads return in
+  // order: the wait for Q leaves these in flight).
   if (it0 < n_tiles) {
     load_k(it0);
     load_v(it0);
@@ -543,14 +565,27 @@ void fwd_bf16_kernel(FwdParams p) {
       const int t = wrow0 + nb * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
+        float2 sc[4];
+        if constexpr (kQTab) {
+          const float4* tp = reinterpret_cast<const float4*>(qtab + (t - qb * RH) * kTabStride + ks * 8 + g * 4);
+          const float4 a = tp[0], b = tp[1];
+          sc[0] = make_float2(a.x, a.y);
+          sc[1] = make_float2(a.z, a.w);
+          sc[2] = make_float2(b.x, b.y);
+          sc[3] = make_float2(b.z, b.w);
+        }
         u32x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float x0 = bf16_lo(qraw[nb][ks][e]), x1 = bf16_hi(qraw[nb][ks][e]);
           if constexpr (ROPE) {
-            const float tr = rope_turns(pos + t, ropec_s[ks * 8 + g * 4 + e]);
             float sn, cs;
-            sincos_rev(tr, &sn, &cs);
+            if constexpr (kQTab) {
+              sn = sc[e].x;
+              cs = sc[e].y;
+            } else {
+              sincos_rev(rope_turns(pos + t, ropec_s[ks * 8 + g * 4 + e]), &sn, &cs);
+            }
             const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
             x0 = y0;
             x1 = y1;
