@@ -190,6 +190,17 @@ def cpu_baseline_window(cfg, window, n_kv=2):
                        f"1024-row blocks; {flops:.3e} algorithmic FLOP")
 
 
+def fwd_workspace(q, k, causal, window, cfg):
+    """The forward's workspace, allocated once before timing (False when the library asks for
+    none: the keys are then rotated inside the prefill)."""
+    import torch
+    from exact_transformer_attention_amd import attn_fwd_workspace_bytes
+    B, Hq, T, d = q.shape
+    need = attn_fwd_workspace_bytes(B, Hq, k.shape[1], T, k.shape[2], d, causal, window, cfg["rope_base"],
+                                    cfg["pos"])
+    return torch.empty(need, dtype=torch.uint8, device=q.device) if need else False
+
+
 def window_bench(a):
     """Causal sliding-window prefill on the 8192-token GQA workload (one JSON line)."""
     import torch
@@ -201,9 +212,10 @@ def window_bench(a):
     q, k, v = (t.to(dev) for t in workloads.make_fwd_inputs(**cfg))
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = fwd_workspace(q, k, True, w, cfg)
 
     def run():
-        attn_fwd_window(q, k, v, w, rope_base=cfg["rope_base"], pos=cfg["pos"], out=out, lse=lse)
+        attn_fwd_window(q, k, v, w, rope_base=cfg["rope_base"], pos=cfg["pos"], out=out, lse=lse, workspace=ws)
 
     for _ in range(a.warmup):
         run()
@@ -282,9 +294,10 @@ def config_bench(a, name):
     q, k, v = (t.to(dev) for t in workloads.make_fwd_inputs(**cfg))
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = fwd_workspace(q, k, True, 0, cfg)
 
     def run():
-        attn_fwd(q, k, v, causal=True, rope_base=cfg["rope_base"], pos=cfg["pos"], out=out, lse=lse)
+        attn_fwd(q, k, v, causal=True, rope_base=cfg["rope_base"], pos=cfg["pos"], out=out, lse=lse, workspace=ws)
 
     steps, warmup = a.steps, a.warmup
     if name == "gqa32k":  # each launch is ~8 ms: fewer launches keep the run short
@@ -607,6 +620,7 @@ def main():
         qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
         out = torch.empty_like(qd)
         lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+        pws = fwd_workspace(qd, kd, pcfg["causal"], 0, pcfg)
     if do_d:
         d = workloads.make_decode_inputs(**dcfg)
         dq = d["q"].to(dev)
@@ -621,7 +635,7 @@ def main():
 
     def prefill():
         attn_fwd(qd, kd, vd, causal=pcfg["causal"], rope_base=pcfg["rope_base"], pos=pcfg["pos"], out=out,
-                 lse=lse)
+                 lse=lse, workspace=pws)
 
     def decode():
         attn_decode_paged(dq, dk, dv, dbt, dsl, block_size=16, rope_base=dcfg["rope_base"], out=dout,

@@ -10,6 +10,7 @@ _BINDING_NAMES = ("ATTN_BF16", "ATTN_ERR_HIP", "ATTN_ERR_INVALID_ARG", "ATTN_ERR
                   "ATTN_ERR_WORKSPACE", "ATTN_F32", "ATTN_OK", "DECODE_STATIC_SCRATCH_BYTES", "EXPORTED", "LIB",
                   "LIB_PATH", "AttnError", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_paged",
                   "attn_decode_paged_static", "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_fp8",
+                  "attn_fwd_workspace_bytes",
                   "attn_fwd_window", "attn_paged_gather", "attn_prefill_paged", "attn_status_str")
 
 __all__ = list(_BINDING_NAMES)

@@ -17,7 +17,7 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ER
 DECODE_STATIC_SCRATCH_BYTES = 32 << 20
 ATTN_F32, ATTN_BF16 = 0, 1
 
-EXPORTED = ("attn_fwd", "attn_fwd_window", "attn_fwd_fp8", "attn_prefill_paged", "attn_decode_paged",
+EXPORTED = ("attn_fwd", "attn_fwd_window", "attn_fwd_workspace_bytes", "attn_fwd_fp8", "attn_prefill_paged", "attn_decode_paged",
             "attn_decode_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes", "attn_paged_gather",
             "attn_status_str")
 
@@ -33,10 +33,13 @@ def _load():
     import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
-    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i64, i32, vp]
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i64, vp, sz, i32, vp]
     lib.attn_fwd.restype = i32
-    lib.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, f32, i64, i32, vp]
+    lib.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, f32, i64, vp, sz, i32,
+                                    vp]
     lib.attn_fwd_window.restype = i32
+    lib.attn_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, f32, i64, i32]
+    lib.attn_fwd_workspace_bytes.restype = sz
     lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp,
                                        i32, vp]
     lib.attn_prefill_paged.restype = i32
@@ -161,24 +164,58 @@ def _paged_args(q, k_cache, v_cache, block_table, seq_lens, block_size, qdim):
     _require(block_table.shape[0] == N, "block_table must have one row per sequence")
 
 
+def attn_fwd_workspace_bytes(B, Hq, Hkv, T, S, d_h, causal=False, window=0, rope_base=0.0, pos=0,
+                             dtype_code=ATTN_BF16):
+    return int(LIB.attn_fwd_workspace_bytes(B, Hq, Hkv, T, S, d_h, int(bool(causal)), int(window),
+                                            float(rope_base), int(pos), dtype_code))
+
+
+def _fwd_workspace(q, workspace, dims, causal, window, rope_base, pos):
+    """The workspace argument of attn_fwd / attn_fwd_window as (pointer, bytes): None asks the
+    library (a buffer is allocated here when it wants one), False passes none, a 1-D device
+    tensor is passed as it is."""
+    import torch
+    B, Hq, Hkv, T, S, d = dims
+    if workspace is False:
+        return None, 0
+    if workspace is None:
+        need = attn_fwd_workspace_bytes(B, Hq, Hkv, T, S, d, causal, window, rope_base, pos, _dtype_code(q))
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _tensor(workspace, "workspace", dim=1)
+    _on_device((("q", q), ("workspace", workspace)))
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def attn_fwd(q, k, v, causal=False, rope_base=0.0, pos=0, out=None, lse=None, want_lse=True,
-             stream=None):
+             workspace=None, stream=None):
     """Exact attention.  q [B,Hq,T,d_h], k/v [B,Hkv,S,d_h] contiguous device tensors of one
     dtype (bf16 or fp32).  Returns (out, lse) with out like q and lse fp32 [B,Hq,T]
-    (None if want_lse is False and no lse buffer was given)."""
-    out, lse, (B, Hq, Hkv, T, S, d) = _fwd_buffers(q, k, v, out, lse, want_lse)
+    (None if want_lse is False and no lse buffer was given).  workspace: None (one is
+    allocated here when attn_fwd_workspace_bytes asks for it: the keys are then rotated once
+    ahead of the prefill), False (none: keys rotated inside the prefill), or a 1-D device
+    tensor (used when it holds B*Hkv*S*d_h*2 bytes)."""
+    out, lse, dims = _fwd_buffers(q, k, v, out, lse, want_lse)
+    B, Hq, Hkv, T, S, d = dims
+    ws, ws_bytes = _fwd_workspace(q, workspace, dims, causal, 0, rope_base, pos)
     st = LIB.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, T, S, d,
-                      int(bool(causal)), float(rope_base), int(pos), _dtype_code(q), _stream(stream))
+                      int(bool(causal)), float(rope_base), int(pos), _ptr(ws), ws_bytes, _dtype_code(q),
+                      _stream(stream))
     _check(st, "attn_fwd")
     return out, lse
 
 
-def attn_fwd_window(q, k, v, window, rope_base=0.0, pos=0, out=None, lse=None, want_lse=True, stream=None):
+def attn_fwd_window(q, k, v, window, rope_base=0.0, pos=0, out=None, lse=None, want_lse=True, workspace=None,
+                    stream=None):
     """Causal sliding-window attention: query row t sees keys pos + t - window < s <= pos + t.
-    Same tensors and results as attn_fwd."""
-    out, lse, (B, Hq, Hkv, T, S, d) = _fwd_buffers(q, k, v, out, lse, want_lse)
+    Same tensors, workspace and results as attn_fwd."""
+    out, lse, dims = _fwd_buffers(q, k, v, out, lse, want_lse)
+    B, Hq, Hkv, T, S, d = dims
+    ws, ws_bytes = _fwd_workspace(q, workspace, dims, True, window, rope_base, pos)
     st = LIB.attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, T, S, d,
-                             int(window), float(rope_base), int(pos), _dtype_code(q), _stream(stream))
+                             int(window), float(rope_base), int(pos), _ptr(ws), ws_bytes, _dtype_code(q),
+                             _stream(stream))
     _check(st, "attn_fwd_window")
     return out, lse
 

@@ -3,6 +3,7 @@
 // untouched.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -47,11 +48,46 @@ const char* attn_status_str(attn_status_t s) {
 
 namespace {
 
+// Rows per workgroup of one head in the bf16 prefill (the kernel's 256 query rows shared by
+// the heads of a group of HP = 4, 2 or 1 query heads) and keys per block.
+constexpr int kPrefillRows = 256;
+constexpr int kKeyBlock = 64;
+
+// Average number of workgroups of the bf16 prefill that read each K block: a K block
+// rotated as it lands is rotated that many times.
+double key_block_reads(int Hq, int Hkv, int T, int S, int causal, int64_t window, int64_t pos) {
+  const int G = Hq / Hkv;
+  const int HP = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+  const int RH = kPrefillRows / HP;
+  const long long nqb = (T + RH - 1) / RH;
+  double tiles = 0.0;
+  for (long long qb = 0; qb < nqb; ++qb) {
+    long long nk = S;
+    if (causal) {
+      const long long last = std::min<long long>(T - 1, qb * RH + RH - 1);
+      nk = std::max<long long>(0, std::min<long long>(S, pos + last + 1));
+    }
+    long long it0 = 0;
+    if (window > 0) {
+      const long long lo = pos + qb * RH - window + 1;
+      it0 = (lo <= 0 ? 0 : std::min(lo, nk)) / kKeyBlock;
+    }
+    tiles += (double)((nk + kKeyBlock - 1) / kKeyBlock - it0);
+  }
+  const long long nkb = (S + kKeyBlock - 1) / kKeyBlock;
+  return tiles * (double)(G / HP) / (double)nkb;
+}
+
+// Rotating the keys ahead pays once a K block is read by about ten workgroups (one extra
+// read and write of k against the rotation work saved); 16 leaves a margin.
+constexpr double kRotateAheadReads = 16.0;
+
 attn_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
                        int T, int S, int d_h, int causal, int64_t window, float rope_base, int64_t pos,
-                       attn_dtype_t dtype, void* stream) {
+                       void* workspace, size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
   if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) || misaligned(lse, 4))
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) || misaligned(lse, 4) ||
+      misaligned(workspace, 16))
     return ATTN_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || d_h < 1) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
@@ -80,6 +116,9 @@ attn_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, f
   p.pos = pos;
   p.use_rope = rope_base > 0.f;
   fill_rope(p.rope_c, d_h, p.use_rope ? rope_base : 1.f);
+  // a workspace large enough for a rotated copy of k: the keys are rotated once, ahead
+  const size_t kbytes = (size_t)B * Hkv * S * d_h * 2;
+  if (dtype == ATTN_BF16 && p.use_rope && workspace && workspace_bytes >= kbytes) p.k_rot = workspace;
 
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = (dtype == ATTN_F32) ? attn::launch_fwd_f32(p, d_h, st) : attn::launch_fwd_bf16(p, d_h, st);
@@ -92,16 +131,30 @@ extern "C" {
 
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
                        int Hkv, int T, int S, int d_h, int causal, float rope_base, int64_t pos,
-                       attn_dtype_t dtype, void* stream) {
-  return fwd_impl(q, k, v, out, lse, B, Hq, Hkv, T, S, d_h, causal, 0, rope_base, pos, dtype, stream);
+                       void* workspace, size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
+  return fwd_impl(q, k, v, out, lse, B, Hq, Hkv, T, S, d_h, causal, 0, rope_base, pos, workspace,
+                  workspace_bytes, dtype, stream);
 }
 
 attn_status_t attn_fwd_window(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                               int Hq, int Hkv, int T, int S, int d_h, int64_t window, float rope_base,
-                              int64_t pos, attn_dtype_t dtype, void* stream) {
+                              int64_t pos, void* workspace, size_t workspace_bytes, attn_dtype_t dtype,
+                              void* stream) {
   if (window < 1) return ATTN_ERR_INVALID_ARG;
   if (window > ((int64_t)1 << 41)) window = (int64_t)1 << 41;  // wider than any reach: plain causal
-  return fwd_impl(q, k, v, out, lse, B, Hq, Hkv, T, S, d_h, 1, window, rope_base, pos, dtype, stream);
+  return fwd_impl(q, k, v, out, lse, B, Hq, Hkv, T, S, d_h, 1, window, rope_base, pos, workspace,
+                  workspace_bytes, dtype, stream);
+}
+
+size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int T, int S, int d_h, int causal, int64_t window,
+                                float rope_base, int64_t pos, attn_dtype_t dtype) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || Hq % Hkv != 0) return 0;
+  if (d_h != 64 && d_h != 128) return 0;
+  if (dtype != ATTN_BF16 || bad_base(rope_base) || !(rope_base > 0.f)) return 0;
+  if (causal != 0 && causal != 1) return 0;
+  if (window > 0) causal = 1;
+  if (key_block_reads(Hq, Hkv, T, S, causal, window, pos) < kRotateAheadReads) return 0;
+  return (size_t)B * Hkv * S * d_h * 2;
 }
 
 attn_status_t attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* out, float* lse, int B, int Hq,

@@ -80,16 +80,48 @@ using prefill::cmul;
 using prefill::max3;
 using prefill::vswz;
 
+// Where the prefill kernel takes its keys from.
+constexpr int kKeysIn = 0;       // the k tensor; with RoPE rotated as each block lands
+constexpr int kKeysPaged = 1;    // a block-tabled cache, already rotated
+constexpr int kKeysRotated = 2;  // a copy of k rotated ahead of the kernel (rope_k_kernel)
+
 }  // namespace
 
-// PAGED: K and V come from a block-tabled cache ([blocks, Hkv, 16, D], as the decode
-// kernels read it), sequence b holding seq_lens[b] tokens whose last T are the queries;
-// cached K is already rotated, so only Q is rotated (at its positions).
-template <int D, int HP, bool ROPE, bool PAGED>
+// Keys rotated ahead of the prefill: k'[b, kvh, s] = RoPE(k[b, kvh, s]) at position s, in
+// the layout of k.  One 16-byte chunk (4 pairs) per thread; the angles are reduced in fp64
+// per element ("How does Rotary Position Embedding (RoPE) work?").  A K block is read by
+// every query block of its group, so rotating it once here beats rotating it in each of
+// them when there are enough of them (the host decides).
+template <int D>
+__global__ __launch_bounds__(256) void rope_k_kernel(const __bf16* __restrict__ k, __bf16* __restrict__ kr,
+                                                     long long n_chunks, int S, FwdParams p) {
+  constexpr int CPR = D / 8;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_chunks) return;
+  const int c = (int)(i % CPR);
+  const int64_t ps = (i / CPR) % S;
+  const u32x4 raw = *(const u32x4*)(k + i * 8);
+  u32x4 outv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float sn, cs;
+    sincos_rev(rope_turns(ps, p.rope_c[c * 4 + e]), &sn, &cs);
+    const float x0 = bf16_lo(raw[e]), x1 = bf16_hi(raw[e]);
+    outv[e] = pack_bf16(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+  }
+  *(u32x4*)(kr + i * 8) = outv;
+}
+
+// KSRC (where the keys come from): kKeysIn, kKeysRotated, or kKeysPaged: K and V from a
+// block-tabled cache ([blocks, Hkv, 16, D], as the decode kernels read it), sequence b
+// holding seq_lens[b] tokens whose last T are the queries.  Cached and pre-rotated K are
+// used as they are; Q is rotated (at its positions) whenever ROPE.
+template <int D, int HP, bool ROPE, int KSRC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kNW / 4, kNW / 4)))
 void fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<D>;
-  constexpr bool ROTK = ROPE && !PAGED;  // rotate K at load
+  constexpr bool PAGED = KSRC == kKeysPaged;
+  constexpr bool ROTK = ROPE && KSRC == kKeysIn;  // rotate K at load
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][kBN * C::KSTR];   // rotated K, padded rows
   __shared__ __attribute__((aligned(16))) u32x4 Vs[2][kBN * C::CPR];     // V, swizzled 16-byte chunks
   __shared__ __attribute__((aligned(16))) u32x4 Kraw[2][kBN * C::CPR];   // K as loaded
@@ -643,7 +675,7 @@ void fwd_bf16_kernel(FwdParams p) {
 }
 
 namespace {
-template <int D, int HP, bool ROPE, bool PAGED>
+template <int D, int HP, bool ROPE, int KSRC>
 hipError_t launch_one(FwdParams q, hipStream_t stream) {
   constexpr int RH = kNW * kQW / HP;
   q.n_qblocks = (q.T + RH - 1) / RH;
@@ -651,7 +683,7 @@ hipError_t launch_one(FwdParams q, hipStream_t stream) {
   q.xcd_remap = work_order_mode(q.n_qblocks, q.n_groups);
   const long long grid = (long long)q.n_qblocks * q.n_groups;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, HP, ROPE, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, HP, ROPE, KSRC>), dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 
@@ -659,9 +691,20 @@ template <int D, int HP>
 hipError_t launch_r(const FwdParams& p, hipStream_t stream) {
   if constexpr (D == 128) {
     if (p.paged)
-      return p.use_rope ? launch_one<D, HP, true, true>(p, stream) : launch_one<D, HP, false, true>(p, stream);
+      return p.use_rope ? launch_one<D, HP, true, kKeysPaged>(p, stream)
+                        : launch_one<D, HP, false, kKeysPaged>(p, stream);
   }
-  return p.use_rope ? launch_one<D, HP, true, false>(p, stream) : launch_one<D, HP, false, false>(p, stream);
+  if (p.use_rope && p.k_rot) {
+    // rotate the keys once, then run the prefill on the rotated copy
+    FwdParams q = p;
+    const long long n_chunks = (long long)p.B * p.Hkv * p.S * (D / 8);
+    if ((n_chunks + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(rope_k_kernel<D>, dim3((unsigned)((n_chunks + 255) / 256)), dim3(256), 0, stream,
+                       (const __bf16*)p.k, (__bf16*)p.k_rot, n_chunks, p.S, p);
+    q.k = p.k_rot;
+    return launch_one<D, HP, true, kKeysRotated>(q, stream);
+  }
+  return p.use_rope ? launch_one<D, HP, true, kKeysIn>(p, stream) : launch_one<D, HP, false, kKeysIn>(p, stream);
 }
 
 template <int D>

@@ -19,6 +19,8 @@ struct FwdParams {
   int causal;
   int use_rope;
   int64_t window;  // > 0: causal sliding window, key s visible iff pos + t - window < s <= pos + t
+  void* k_rot;     // bf16 with RoPE: [B, Hkv, S, d_h] buffer for k rotated ahead of the kernel, or
+                   // null (k rotated as its blocks land)
   // paged prefill (k, v are block-tabled caches [blocks, Hkv, 16, d_h]; S and pos per sequence)
   int paged;
   const int32_t* block_table;  // [B, max_blocks_per_seq]

@@ -67,6 +67,14 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
  *            work?"); query row t sits at position pos + t, key s at position s.
  *            0 disables the rotation.
  *   pos      absolute position of query row 0 (0 for self-attention over a prompt)
+ *   workspace, workspace_bytes  optional device scratch (16-byte aligned), caller-owned, no
+ *            clearing needed; overlapping calls must not share one.  With bf16, RoPE and at
+ *            least B * Hkv * S * d_h * 2 bytes, k is rotated once into it by a first kernel
+ *            and the prefill reads that copy; otherwise (NULL, smaller, fp32 or no RoPE) each
+ *            key block is rotated as it lands in the prefill, once per query block that reads
+ *            it.  attn_fwd_workspace_bytes says when the first pays.  Same definition either
+ *            way; the rotated keys are rounded to bf16 from slightly different angle
+ *            arithmetic, so the two results may differ in the last bits.
  *   dtype    ATTN_F32 or ATTN_BF16 (bf16 inputs use bf16 MFMA with fp32 accumulation)
  *
  * Supported: d_h in {64, 128}; any B, Hq, Hkv >= 1 with Hq % Hkv == 0; any
@@ -76,7 +84,19 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
  */
 ATTN_API attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                        int B, int Hq, int Hkv, int T, int S, int d_h, int causal,
-                       float rope_base, int64_t pos, attn_dtype_t dtype, void* stream);
+                       float rope_base, int64_t pos, void* workspace, size_t workspace_bytes,
+                       attn_dtype_t dtype, void* stream);
+
+/*
+ * Bytes of workspace worth giving attn_fwd (window 0) or attn_fwd_window (window >= 1)
+ * for these sizes: B * Hkv * S * d_h * 2 when the keys are better rotated once ahead of the
+ * prefill (bf16 with RoPE, and each key block read by at least 16 of the prefill's
+ * workgroups of 256 query rows, so that the extra pass over k costs less than the repeated
+ * rotation); 0 when not, or on invalid sizes.
+ */
+ATTN_API size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int T, int S, int d_h, int causal,
+                                         int64_t window, float rope_base, int64_t pos,
+                                         attn_dtype_t dtype);
 
 /*
  * attn_fwd_window -- causal sliding-window attention: key s is visible to query row t
@@ -86,13 +106,14 @@ ATTN_API attn_status_t attn_fwd(const void* q, const void* k, const void* v, voi
  * size w, cost O(n w); "Why is attention O(n^2) ...", Long context in practice: sliding
  * window of width w, O(T w)).  Key blocks outside the window are not visited.
  *
- * Arguments, layouts, RoPE and the result are as for attn_fwd with causal = 1;
- * window >= 1 (ATTN_ERR_INVALID_ARG otherwise), and a window reaching back past key 0
- * gives exactly the causal result.
+ * Arguments, layouts, RoPE, the workspace and the result are as for attn_fwd with
+ * causal = 1; window >= 1 (ATTN_ERR_INVALID_ARG otherwise), and a window reaching back past
+ * key 0 gives exactly the causal result.
  */
 ATTN_API attn_status_t attn_fwd_window(const void* q, const void* k, const void* v, void* out,
                                        float* lse, int B, int Hq, int Hkv, int T, int S, int d_h,
                                        int64_t window, float rope_base, int64_t pos,
+                                       void* workspace, size_t workspace_bytes,
                                        attn_dtype_t dtype, void* stream);
 
 /*

@@ -41,10 +41,14 @@ def check_close(got, ref, dtype, what, lse_got=None, lse_ref=None):
     return ma, rr
 
 
-def run_fwd_gpu(q, k, v, causal, rope_base, pos):
+def run_fwd_gpu(q, k, v, causal, rope_base, pos, workspace=None):
+    """workspace: None (the library's choice), False (keys rotated inside the prefill) or
+    "ahead" (a workspace for the rotated keys, whatever the sizes)."""
     from exact_transformer_attention_amd import attn_fwd
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    out, lse = attn_fwd(qd, kd, vd, causal=causal, rope_base=rope_base, pos=pos)
+    if isinstance(workspace, str):
+        workspace = torch.empty(kd.numel() * 2, dtype=torch.uint8, device=kd.device)
+    out, lse = attn_fwd(qd, kd, vd, causal=causal, rope_base=rope_base, pos=pos, workspace=workspace)
     torch.cuda.synchronize()
     return out, lse
 

@@ -24,7 +24,7 @@ def lib():
 
 def test_header_declares_entry_points():
     names = header_functions()
-    assert names == sorted(["attn_fwd", "attn_fwd_window", "attn_fwd_fp8", "attn_prefill_paged", "attn_decode_paged",
+    assert names == sorted(["attn_fwd", "attn_fwd_window", "attn_fwd_workspace_bytes", "attn_fwd_fp8", "attn_prefill_paged", "attn_decode_paged",
                             "attn_decode_paged_static", "attn_decode_workspace_bytes", "attn_bwd",
                             "attn_bwd_workspace_bytes", "attn_paged_gather", "attn_status_str"])
 
@@ -52,10 +52,10 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails va
 
 def fwd(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, B=1, Hq=4, Hkv=2, T=8, S=8, d=128, causal=1,
-             base=10000.0, pos=0, dtype=1)
+             base=10000.0, pos=0, ws=None, wsb=0, dtype=1)
     a.update(kw)
     return lib.attn_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["T"], a["S"],
-                        a["d"], a["causal"], a["base"], a["pos"], a["dtype"], None)
+                        a["d"], a["causal"], a["base"], a["pos"], a["ws"], a["wsb"], a["dtype"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -66,6 +66,8 @@ def fwd(lib, **kw):
     (dict(d=96), 2), (dict(d=256), 2), (dict(pos=1 << 41), 2),
     # one KV head's bf16 keys past a 32-bit byte range (S * d_h * 2 >= 2^32)
     (dict(S=1 << 24), 2), (dict(S=1 << 25, d=64), 2),
+    # a workspace must be 16-byte aligned (the rotated keys are moved in 16-byte chunks)
+    (dict(ws=ctypes.c_void_p(0x1008), wsb=1 << 20), 1),
 ])
 def test_fwd_validation(lib, kw, status):
     assert fwd(lib, **kw) == status
@@ -73,18 +75,54 @@ def test_fwd_validation(lib, kw, status):
 
 def fwd_window(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, B=1, Hq=4, Hkv=2, T=8, S=8, d=128, window=16,
-             base=10000.0, pos=0, dtype=1)
+             base=10000.0, pos=0, ws=None, wsb=0, dtype=1)
     a.update(kw)
     return lib.attn_fwd_window(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["T"],
-                               a["S"], a["d"], a["window"], a["base"], a["pos"], a["dtype"], None)
+                               a["S"], a["d"], a["window"], a["base"], a["pos"], a["ws"], a["wsb"], a["dtype"],
+                               None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(window=0), 1), (dict(window=-3), 1), (dict(q=None), 1), (dict(Hq=6, Hkv=4), 1), (dict(dtype=9), 1),
-    (dict(d=96), 2), (dict(pos=1 << 41), 2),
+    (dict(d=96), 2), (dict(pos=1 << 41), 2), (dict(ws=ctypes.c_void_p(0x1004), wsb=1 << 20), 1),
 ])
 def test_fwd_window_validation(lib, kw, status):
     assert fwd_window(lib, **kw) == status
+
+
+def kbytes(B, Hkv, S, d):
+    return B * Hkv * S * d * 2
+
+
+@pytest.mark.parametrize("args,expect", [
+    # 2 x 32 query heads over 8 KV heads, 8192 causal tokens, RoPE: each K block is read by
+    # about 64 workgroups of 4 heads x 64 rows -> rotate once ahead
+    (dict(B=2, Hq=32, Hkv=8, T=8192, S=8192, causal=1), kbytes(2, 8, 8192, 128)),
+    (dict(B=1, Hq=32, Hkv=8, T=32768, S=32768, causal=1), kbytes(1, 8, 32768, 128)),
+    # the same with a 4096-key window: still ~64 readers per block
+    (dict(B=2, Hq=32, Hkv=8, T=8192, S=8192, causal=1, window=4096), kbytes(2, 8, 8192, 128)),
+    # no grouping, 2048 tokens: workgroups of 256 rows of one head, ~4.5 readers per block
+    (dict(B=4, Hq=32, Hkv=32, T=2048, S=2048, causal=1), 0),
+    # 1024 grouped tokens: 16 query blocks of which ~8.5 read each K block
+    (dict(B=1, Hq=32, Hkv=8, T=1024, S=1024, causal=1), 0),
+    # non-causal: every query block reads every K block (16 of them at 1024 rows / 64)
+    (dict(B=1, Hq=8, Hkv=2, T=1024, S=512, causal=0), kbytes(1, 2, 512, 128)),
+    (dict(B=1, Hq=8, Hkv=2, T=960, S=512, causal=0), 0),
+    # d_h 64 is sized the same way
+    (dict(B=1, Hq=8, Hkv=2, T=1024, S=512, causal=0, d=64), kbytes(1, 2, 512, 64)),
+    # no RoPE, fp32, or invalid sizes: nothing to rotate ahead
+    (dict(B=2, Hq=32, Hkv=8, T=8192, S=8192, causal=1, base=0.0), 0),
+    (dict(B=2, Hq=32, Hkv=8, T=8192, S=8192, causal=1, dtype=0), 0),
+    (dict(B=2, Hq=30, Hkv=8, T=8192, S=8192, causal=1), 0),
+    (dict(B=2, Hq=32, Hkv=8, T=8192, S=8192, causal=1, d=96), 0),
+    (dict(B=0, Hq=32, Hkv=8, T=8192, S=8192, causal=1), 0),
+])
+def test_fwd_workspace_bytes(lib, args, expect):
+    a = dict(causal=1, window=0, base=10000.0, pos=0, dtype=1, d=128)
+    a.update(args)
+    got = lib.attn_fwd_workspace_bytes(a["B"], a["Hq"], a["Hkv"], a["T"], a["S"], a["d"], a["causal"],
+                                       a["window"], a["base"], a["pos"], a["dtype"])
+    assert got == expect
 
 
 def dec(lib, **kw):

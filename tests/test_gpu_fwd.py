@@ -17,11 +17,11 @@ from tolerances import LARGE_LOGITS, OFFSET_LSE, RISING_LSE
 pytestmark = pytest.mark.gpu
 
 
-def full_case(dtype, B, Hq, Hkv, T, S, d_h, causal, rope_base, pos, seed, sigma=1.0):
+def full_case(dtype, B, Hq, Hkv, T, S, d_h, causal, rope_base, pos, seed, sigma=1.0, workspace=None):
     cfg = dict(B=B, Hq=Hq, Hkv=Hkv, T=T, S=S, d_h=d_h, dtype=dtype, sigma=sigma, seed=seed)
-    say(f"case {cfg} causal={causal} rope={rope_base} pos={pos}")
+    say(f"case {cfg} causal={causal} rope={rope_base} pos={pos} workspace={workspace}")
     q, k, v = gen(cfg)
-    out, lse = run_fwd_gpu(q, k, v, causal, rope_base, pos)
+    out, lse = run_fwd_gpu(q, k, v, causal, rope_base, pos, workspace)
     ro, rl = oracle.attention(f64(q), f64(k), f64(v), causal=causal, rope_base=rope_base, pos=pos)
     check_close(f64(out), ro, dtype, "out", f64(lse), rl)
 
@@ -75,6 +75,40 @@ BF16_CASES = [
 def test_bf16_shapes(case):
     B, Hq, Hkv, T, S, d, causal, base, pos = case
     full_case("bf16", B, Hq, Hkv, T, S, d, causal, base, pos, seed=200 + T + S)
+
+
+# Keys rotated once ahead of the prefill (a workspace given whatever the sizes): the RoPE
+# cases above, every head packing and both head sizes.
+AHEAD_CASES = [c for c in BF16_CASES if c[7] > 0]
+
+
+@pytest.mark.parametrize("case", AHEAD_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bf16_keys_rotated_ahead(case):
+    B, Hq, Hkv, T, S, d, causal, base, pos = case
+    full_case("bf16", B, Hq, Hkv, T, S, d, causal, base, pos, seed=200 + T + S, workspace="ahead")
+
+
+def test_bf16_workspace_use():
+    """The rotated copy is rebuilt on every call (a poisoned workspace changes nothing); a
+    workspace too small for it, or none, runs the rotation inside the prefill (the same bits
+    as with no workspace); the library asks for one only when each key block has many readers."""
+    from exact_transformer_attention_amd import attn_fwd, attn_fwd_workspace_bytes
+    cfg = dict(B=1, Hq=8, Hkv=2, T=700, S=700, d_h=128, dtype="bf16", sigma=1.0, seed=4242)
+    q, k, v = (t.cuda() for t in gen(cfg))
+    need = k.numel() * 2
+    ws = torch.full((need + 4096,), 0xFF, dtype=torch.uint8, device="cuda")
+    o1, l1 = attn_fwd(q, k, v, causal=True, rope_base=10000.0, workspace=ws)
+    ws.fill_(0x7F)
+    o2, l2 = attn_fwd(q, k, v, causal=True, rope_base=10000.0, workspace=ws)
+    o3, l3 = attn_fwd(q, k, v, causal=True, rope_base=10000.0, workspace=False)
+    o4, l4 = attn_fwd(q, k, v, causal=True, rope_base=10000.0, workspace=ws[:need - 16])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
+    assert attn_fwd_workspace_bytes(1, 8, 2, 700, 700, 128, True, 0, 10000.0, 0) == 0
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), causal=True, rope_base=10000.0, pos=0)
+    check_close(f64(o1), ro, "bf16", "out (rotated ahead)", f64(l1), rl)
+    check_close(f64(o3), ro, "bf16", "out (rotated in the prefill)", f64(l3), rl)
 
 
 def test_bf16_fully_masked_rows():

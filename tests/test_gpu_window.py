@@ -13,9 +13,12 @@ from gpu_common import check_close, f64, gen, say
 pytestmark = pytest.mark.gpu
 
 
-def run_window(q, k, v, window, rope_base, pos):
+def run_window(q, k, v, window, rope_base, pos, workspace=None):
     from exact_transformer_attention_amd import attn_fwd_window
-    out, lse = attn_fwd_window(q.cuda(), k.cuda(), v.cuda(), window, rope_base=rope_base, pos=pos)
+    if workspace == "ahead":  # a workspace for keys rotated ahead, whatever the sizes
+        workspace = torch.empty(k.numel() * 2, dtype=torch.uint8, device="cuda")
+    out, lse = attn_fwd_window(q.cuda(), k.cuda(), v.cuda(), window, rope_base=rope_base, pos=pos,
+                               workspace=workspace)
     torch.cuda.synchronize()
     return out, lse
 
@@ -45,6 +48,18 @@ def test_window_shapes(case):
     say(f"window case {case}")
     q, k, v = gen(cfg)
     out, lse = run_window(q, k, v, w, base, pos)
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), causal=True, rope_base=base, pos=pos, window=w)
+    check_close(f64(out), ro, dtype, f"window {w}", f64(lse), rl)
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if c[0] == "bf16" and c[8] > 0],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_window_keys_rotated_ahead(case):
+    dtype, B, Hq, Hkv, T, S, d, w, base, pos = case
+    cfg = dict(B=B, Hq=Hq, Hkv=Hkv, T=T, S=S, d_h=d, dtype=dtype, seed=300 + T + w % 97)
+    say(f"window case {case}, keys rotated ahead")
+    q, k, v = gen(cfg)
+    out, lse = run_window(q, k, v, w, base, pos, workspace="ahead")
     ro, rl = oracle.attention(f64(q), f64(k), f64(v), causal=True, rope_base=base, pos=pos, window=w)
     check_close(f64(out), ro, dtype, f"window {w}", f64(lse), rl)
 
