@@ -122,9 +122,19 @@ void fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<D>;
   constexpr bool PAGED = KSRC == kKeysPaged;
   constexpr bool ROTK = ROPE && KSRC == kKeysIn;  // rotate K at load
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][kBN * C::KSTR];   // rotated K, padded rows
+  // K copied by the loads straight into its operand tile (no rotation in the kernel, keys
+  // not paged); otherwise K lands in Kraw and each thread moves (rotates) its chunks.
+  constexpr bool KDIRECT = !ROTK && !PAGED;
+  // K operand tiles (padded rows) of the two blocks in flight: two arrays, so that reads of
+  // one are never held up by the compiler for loads into the other
+  __shared__ __attribute__((aligned(16))) __bf16 Ks0[kBN * C::KSTR];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks1[kBN * C::KSTR];
   __shared__ __attribute__((aligned(16))) u32x4 Vs[2][kBN * C::CPR];     // V, swizzled 16-byte chunks
-  __shared__ __attribute__((aligned(16))) u32x4 Kraw[2][kBN * C::CPR];   // K as loaded
+  __shared__ __attribute__((aligned(16))) u32x4 Kraw[KDIRECT ? 1 : 2][kBN * C::CPR];  // K as loaded
+  auto ks_tile = [&](auto bc) -> __bf16* {
+    if constexpr (decltype(bc)::value == 0) return Ks0;
+    else return Ks1;
+  };
   __shared__ int32_t tbl[PAGED ? kMaxPagedBlocks : 1];                     // block table row
 
   const int tid = threadIdx.x;
@@ -260,6 +270,26 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int j = 0; j < C::NCH; ++j)
       buffer_load_lds16(rs, koff[j], &Kraw[tile & 1][(wid * C::NCH + j) * kWave]);
   };
+  // Direct K: the padded operand tile of a block, copied in 1 KB pieces (piece n by wave
+  // n % kNW, lane i taking its bytes 16i..16i+15).  Lanes that fall on row padding read a
+  // chunk of their row again (the padding is never read back).
+  constexpr int kPieces = kBN * C::KSTR * 2 / 1024;
+  constexpr int kPiecesPerWave = (kPieces + kNW - 1) / kNW;
+  static_assert(kPieces * 1024 == kBN * C::KSTR * 2, "whole pieces");
+  int kdoff[kPiecesPerWave];
+#pragma unroll
+  for (int j = 0; j < kPiecesPerWave; ++j) {
+    const int o = (wid + kNW * j) * 1024 + lane * 16;
+    const int row = o / (C::KSTR * 2), cb = o % (C::KSTR * 2);
+    kdoff[j] = row * D * 2 + (cb < D * 2 ? cb : 0);
+  }
+  auto load_k_direct = [&](int tile, auto bc) {
+    const i32x4 rs = block_rsrc(kg, tile * kBN);
+    char* dst = (char*)ks_tile(bc);
+#pragma unroll
+    for (int j = 0; j < kPiecesPerWave; ++j)
+      if (wid + kNW * j < kPieces) buffer_load_lds16(rs, kdoff[j], dst + (wid + kNW * j) * 1024);
+  };
   auto load_v = [&](int tile) {
     if constexpr (PAGED) {
 #pragma unroll
@@ -296,14 +326,14 @@ void fwd_bf16_kernel(FwdParams p) {
           out[e] = pack_bf16(x0 * c[e] - x1 * s[e], x0 * s[e] + x1 * c[e]);
           if (j + 1 < C::NCH) cmul(c[e], s[e], rc[e], rs[e]);
         }
-        *(u32x4*)&Ks[kb][(row0 + j * C::RSTEP) * C::KSTR + slot * 8] = out;
+        *(u32x4*)&ks_tile(kbc)[(row0 + j * C::RSTEP) * C::KSTR + slot * 8] = out;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) cmul(ac[e], as[e], tc[e], ts[e]);
     } else {
 #pragma unroll
       for (int j = 0; j < C::NCH; ++j)
-        *(u32x4*)&Ks[kb][(row0 + j * C::RSTEP) * C::KSTR + slot * 8] = raw_in[j];
+        *(u32x4*)&ks_tile(kbc)[(row0 + j * C::RSTEP) * C::KSTR + slot * 8] = raw_in[j];
     }
   };
   // Exact angles of this thread's first key of block `tile` (every kResync blocks; the
@@ -389,17 +419,19 @@ void fwd_bf16_kernel(FwdParams p) {
         for (int nb = 0; nb < kNB; ++nb)
           s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][mb], qop[nb][ks], s[mb][nb], 0, 0, 0);
       // rotation unit ks: pair slot e of chunk j
-      const int j = ks / 4, e = ks % 4;
-      if constexpr (ROTK) {
-        const float x0 = bf16_lo(raw[j][e]), x1 = bf16_hi(raw[j][e]);
-        out[j][e] = pack_bf16(x0 * c[e] - x1 * sn[e], x0 * sn[e] + x1 * c[e]);
-        if (j + 1 < C::NCH) cmul(c[e], sn[e], rc[e], rs[e]);
-        else cmul(ac[e], as[e], tc[e], ts[e]);
-      } else {
-        out[j][e] = raw[j][e];
+      if constexpr (!KDIRECT) {
+        const int j = ks / 4, e = ks % 4;
+        if constexpr (ROTK) {
+          const float x0 = bf16_lo(raw[j][e]), x1 = bf16_hi(raw[j][e]);
+          out[j][e] = pack_bf16(x0 * c[e] - x1 * sn[e], x0 * sn[e] + x1 * c[e]);
+          if (j + 1 < C::NCH) cmul(c[e], sn[e], rc[e], rs[e]);
+          else cmul(ac[e], as[e], tc[e], ts[e]);
+        } else {
+          out[j][e] = raw[j][e];
+        }
+        if (e == 3) *(u32x4*)&ks_tile(kbc)[(row0 + j * C::RSTEP) * C::KSTR + slot * 8] = out[j];
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (e == 3) *(u32x4*)&Ks[kn][(row0 + j * C::RSTEP) * C::KSTR + slot * 8] = out[j];
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // exp2 of one 32-key half for both n-blocks -> bf16 P operands and this half's row sums.
@@ -461,22 +493,29 @@ void fwd_bf16_kernel(FwdParams p) {
     // This thread's raw K chunks of block it+1 are read before any load is issued, and raw
     // K of block it+2 is only requested once the product of block it has read its
     // operands: the compiler cannot tell the LDS buffers apart and would otherwise wait
-    // for the loads in flight to land before those reads.
+    // for the loads in flight to land before those reads.  Direct K of block it+1 goes
+    // straight into the other operand tile.
     u32x4 raw[C::NCH];
+    if constexpr (!KDIRECT) {
 #pragma unroll
-    for (int j = 0; j < C::NCH; ++j) raw[j] = Kraw[PAR ^ 1][(wid * C::NCH + j) * kWave + lane];
-    if (it + 1 < n_tiles) load_v(it + 1);
+      for (int j = 0; j < C::NCH; ++j) raw[j] = Kraw[PAR ^ 1][(wid * C::NCH + j) * kWave + lane];
+    }
+    if (it + 1 < n_tiles) {
+      load_v(it + 1);
+      if constexpr (KDIRECT) load_k_direct(it + 1, std::integral_constant<int, PAR ^ 1>{});
+    }
     const bool rot = it + 1 < n_tiles;  // rotate block it+1 during this iteration
     if (rot) resync(it + 1);
     const int k0 = it * kBN;
-    const __bf16* kbuf = &Ks[PAR][0];
+    const __bf16* kbuf = ks_tile(par);
     const char* vbuf = (const char*)&Vs[PAR][0];
     if (k0 < nk_wave && (int64_t)(k0 + kBN) > lo_wave) {
       f32x16 s[2][kNB];
       // The rotation of block it+1 is woven into the product; after the last block it
       // rotates stale data into a buffer nobody reads.
       qk_rot(kbuf, s, std::integral_constant<int, PAR ^ 1>{}, raw);
-      if (it + 2 < n_tiles) load_k(it + 2);
+      if constexpr (!KDIRECT)
+        if (it + 2 < n_tiles) load_k(it + 2);
       // mask (diagonal / tail blocks only)
       const bool need_mask = (k0 + kBN > S) || (p.causal && (int64_t)(k0 + kBN - 1) > pos + wrow0) ||
                              (p.window > 0 && (int64_t)k0 < lo_wave + kQW - 1);
@@ -555,7 +594,7 @@ void fwd_bf16_kernel(FwdParams p) {
         pv(vbuf, 2 * mb, pop);
         pv(vbuf, 2 * mb + 1, pop);
       }
-    } else {
+    } else if constexpr (!KDIRECT) {
       if (rot) rotate_k(it + 1, std::integral_constant<int, PAR ^ 1>{}, raw);
       if (it + 2 < n_tiles) load_k(it + 2);
     }
@@ -586,9 +625,15 @@ void fwd_bf16_kernel(FwdParams p) {
   // before the Q rows are waited for, so the two latencies overlap (loads return in
   // order: the wait for Q leaves these in flight).
   if (it0 < n_tiles) {
-    load_k(it0);
+    if constexpr (KDIRECT) {
+      if (it0 & 1) load_k_direct(it0, std::integral_constant<int, 1>{});
+      else load_k_direct(it0, std::integral_constant<int, 0>{});
+    } else {
+      load_k(it0);
+    }
     load_v(it0);
-    if (it0 + 1 < n_tiles) load_k(it0 + 1);
+    if constexpr (!KDIRECT)
+      if (it0 + 1 < n_tiles) load_k(it0 + 1);
   }
   {  // Q: RoPE at its positions and the scale log2(e)/sqrt(d_h), folded into the operand
     const float qscale = kLog2e / sqrtf((float)D);
@@ -637,11 +682,13 @@ void fwd_bf16_kernel(FwdParams p) {
   if (it0 < n_tiles) {
     resync(it0, true);
     wait_loads();
-    u32x4 raw[C::NCH];
+    if constexpr (!KDIRECT) {
+      u32x4 raw[C::NCH];
 #pragma unroll
-    for (int j = 0; j < C::NCH; ++j) raw[j] = Kraw[it0 & 1][(wid * C::NCH + j) * kWave + lane];
-    if (it0 & 1) rotate_k(it0, std::integral_constant<int, 1>{}, raw);
-    else rotate_k(it0, std::integral_constant<int, 0>{}, raw);
+      for (int j = 0; j < C::NCH; ++j) raw[j] = Kraw[it0 & 1][(wid * C::NCH + j) * kWave + lane];
+      if (it0 & 1) rotate_k(it0, std::integral_constant<int, 1>{}, raw);
+      else rotate_k(it0, std::integral_constant<int, 0>{}, raw);
+    }
   }
   int it = it0;
   if (it < n_tiles && (it & 1)) step(std::integral_constant<int, 1>{}, it++);
