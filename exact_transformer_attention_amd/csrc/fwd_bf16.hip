@@ -122,9 +122,9 @@ void fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<D>;
   constexpr bool PAGED = KSRC == kKeysPaged;
   constexpr bool ROTK = ROPE && KSRC == kKeysIn;  // rotate K at load
-  // K copied by the loads straight into its operand tile (no rotation in the kernel, keys
-  // not paged); otherwise K lands in Kraw and each thread moves (rotates) its chunks.
-  constexpr bool KDIRECT = !ROTK && !PAGED;
+  // K copied by the loads straight into its operand tile when the kernel does not rotate
+  // it; otherwise K lands in Kraw and each thread rotates the chunks it loaded.
+  constexpr bool KDIRECT = !ROTK;
   // K operand tiles (padded rows) of the two blocks in flight: two arrays, so that reads of
   // one are never held up by the compiler for loads into the other
   __shared__ __attribute__((aligned(16))) __bf16 Ks0[kBN * C::KSTR];
@@ -284,8 +284,16 @@ void fwd_bf16_kernel(FwdParams p) {
     kdoff[j] = row * D * 2 + (cb < D * 2 ? cb : 0);
   }
   auto load_k_direct = [&](int tile, auto bc) {
-    const i32x4 rs = block_rsrc(kg, tile * kBN);
     char* dst = (char*)ks_tile(bc);
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int j = 0; j < kPiecesPerWave; ++j)
+        if (wid + kNW * j < kPieces)
+          load_lds16(kg + paged_row(tile * kBN + kdoff[j] / (D * 2)) + kdoff[j] % (D * 2) / 2,
+                     dst + (wid + kNW * j) * 1024);
+      return;
+    }
+    const i32x4 rs = block_rsrc(kg, tile * kBN);
 #pragma unroll
     for (int j = 0; j < kPiecesPerWave; ++j)
       if (wid + kNW * j < kPieces) buffer_load_lds16(rs, kdoff[j], dst + (wid + kNW * j) * 1024);
