@@ -99,11 +99,14 @@ def summarize_pmc(fetch_csv, write_csv, out_dir, extra_kind=None):
     w_scale = copy_bytes / w_copy if w_copy else 1.0
     res = {"calibration": {"kernel": "1 GiB device copy", "fetch_raw_bytes": f_copy, "write_raw_bytes": w_copy,
                            "fetch_scale": f_scale, "write_scale": w_scale}}
+    # kernels of one timed call; a name ending in "?" is launched only for some sizes (the
+    # keys rotated ahead of the prefill) and counts zero when absent
+    prefill_kernels = ["fwd_bf16_kernel", "rope_k_kernel?"]
     kinds = (((extra_kind, ["bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"], BWD_SOURCES),)
              if extra_kind == "bwd" else
              ((extra_kind, ["fwd_fp8_kernel"], FP8_SOURCES),) if extra_kind == "fp8" else
-             ((extra_kind, ["fwd_bf16_kernel"], PREFILL_SOURCES),) if extra_kind else
-             (("prefill", ["fwd_bf16_kernel"], PREFILL_SOURCES),
+             ((extra_kind, prefill_kernels, PREFILL_SOURCES),) if extra_kind else
+             (("prefill", prefill_kernels, PREFILL_SOURCES),
               ("decode", ["decode_partial_kernel", "decode_merge_kernel"], DECODE_SOURCES)))
     path = os.path.join(out_dir, "traffic.json")
     if os.path.exists(path):  # entries of the other runs are kept
@@ -112,13 +115,16 @@ def summarize_pmc(fetch_csv, write_csv, out_dir, extra_kind=None):
         old[(extra_kind + "_calibration") if extra_kind else "calibration"] = res["calibration"]
         res = old
     for kind, keys, srcs in kinds:
-        fb = [pick(fetch, k) for k in keys]
-        wb = [pick(write, k) for k in keys]
+        need = [k for k in keys if not k.endswith("?")]
+        opt = [k[:-1] for k in keys if k.endswith("?")]
+        fb = [pick(fetch, k) for k in need]
+        wb = [pick(write, k) for k in need]
         if any(x is None for x in fb + wb):
             continue
-        rd = sum(fb) * f_scale
-        wr = sum(wb) * w_scale
-        res[kind] = {"kernels": keys, "fetch_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+        ran = [k for k in opt if pick(fetch, k) is not None and pick(write, k) is not None]
+        rd = (sum(fb) + sum(pick(fetch, k) for k in ran)) * f_scale
+        wr = (sum(wb) + sum(pick(write, k) for k in ran)) * w_scale
+        res[kind] = {"kernels": need + ran, "fetch_bytes_per_launch": rd, "write_bytes_per_launch": wr,
                      "hbm_bytes_per_launch": rd + wr, "source_digest": kernel_sources_digest(srcs)}
     os.makedirs(out_dir, exist_ok=True)
     with open(path, "w") as f:
@@ -201,6 +207,11 @@ def fwd_workspace(q, k, causal, window, cfg):
     return torch.empty(need, dtype=torch.uint8, device=q.device) if need else False
 
 
+def prefill_kernels(ws, hp):
+    """The kernels of one timed prefill call (the launch duration covers all of them)."""
+    return (f"rope_k_kernel + " if ws is not False else "") + f"fwd_bf16_kernel<128,{hp}>"
+
+
 def window_bench(a):
     """Causal sliding-window prefill on the 8192-token GQA workload (one JSON line)."""
     import torch
@@ -248,7 +259,7 @@ def window_bench(a):
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("window", kernel_sources_digest(PREFILL_SOURCES)),
-                     "kernel": "fwd_bf16_kernel<128,4>", "flop_per_launch": flops, "avg_launch_ms": round(avg, 4)},
+                     "kernel": prefill_kernels(ws, 4), "flop_per_launch": flops, "avg_launch_ms": round(avg, 4)},
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host (window sample)", file=sys.stderr, flush=True)
@@ -336,7 +347,7 @@ def config_bench(a, name):
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(name, kernel_sources_digest(PREFILL_SOURCES)),
-                     "kernel": f"fwd_bf16_kernel<128,{hp}>", "flop_per_launch": flops, "avg_launch_ms": round(avg, 4)},
+                     "kernel": prefill_kernels(ws, hp), "flop_per_launch": flops, "avg_launch_ms": round(avg, 4)},
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_config(name, cfg)
@@ -712,7 +723,7 @@ def main():
             "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic("prefill", kernel_sources_digest(PREFILL_SOURCES)),
-            "kernel": "fwd_bf16_kernel<128,4>", "flop_per_launch": flops, "avg_launch_ms": round(p_avg, 4),
+            "kernel": prefill_kernels(pws, 4), "flop_per_launch": flops, "avg_launch_ms": round(p_avg, 4),
         },
         "decode": {
             "value": round(dec_gbs, 1), "unit": "GB/s", "avg_step_ms": round(d_avg, 4),

@@ -613,17 +613,28 @@ void fwd_bf16_kernel(FwdParams p) {
   // positions, so the (sin, cos) table of those positions is computed once, eight entries
   // per thread, into LDS (rows padded to D/2 + 2 entries), and each lane reads its 32.
   // This runs while the Q rows are in flight.
+  // With fewer heads (HP = 2 or 1: 128 or 256 positions) the angle of position
+  // qb*RH + 16a + b is composed from two tables of (sin, cos), one for the RH/16 positions
+  // qb*RH + 16a and one for the 16 offsets b, both reduced in fp64: the entries computed
+  // drop from 32 per thread to 3 or 4, for one complex product per element.
   constexpr bool kQTab = ROPE && HP == 4 && RH == 64;
+  constexpr bool kQTab2 = ROPE && !kQTab;
   constexpr int kTabStride = D / 2 + 2;  // float2 entries per table row
-  __shared__ __attribute__((aligned(16))) float2 qtab[kQTab ? RH * kTabStride : 1];
-  if constexpr (kQTab) {
+  constexpr int kTabA = RH / 16;         // rows of the coarse table
+  __shared__ __attribute__((aligned(16))) float2 qtab[kQTab ? RH * kTabStride : (kQTab2 ? (kTabA + 16) * kTabStride : 1)];
+  if constexpr (kQTab || kQTab2) {
     const int64_t p0 = pos + (int64_t)qb * RH;
+    constexpr int kRows = kQTab ? RH : kTabA + 16;
 #pragma unroll
-    for (int k = 0; k < RH * (D / 2) / kThreads; ++k) {
+    for (int k = 0; k < (kRows * (D / 2) + kThreads - 1) / kThreads; ++k) {
       const int e = tid + k * kThreads, r = e / (D / 2), i = e % (D / 2);
-      float sn, cs;
-      sincos_rev(rope_turns(p0 + r, ropec_s[i]), &sn, &cs);
-      qtab[r * kTabStride + i] = make_float2(sn, cs);
+      if (r < kRows) {
+        // coarse rows: positions p0 + 16r; fine rows (after kTabA): offsets r - kTabA
+        const int64_t at = kQTab ? p0 + r : (r < kTabA ? p0 + 16 * r : (int64_t)(r - kTabA));
+        float sn, cs;
+        sincos_rev(rope_turns(at, ropec_s[i]), &sn, &cs);
+        qtab[r * kTabStride + i] = make_float2(sn, cs);
+      }
     }
     // before the block copies: a barrier with direct-to-LDS loads in flight waits for them
     __syncthreads();
@@ -658,6 +669,18 @@ void fwd_bf16_kernel(FwdParams p) {
           sc[1] = make_float2(a.z, a.w);
           sc[2] = make_float2(b.x, b.y);
           sc[3] = make_float2(b.z, b.w);
+        } else if constexpr (kQTab2) {
+          const int tl = t - qb * RH;
+          const float4* ta = reinterpret_cast<const float4*>(qtab + (tl >> 4) * kTabStride + ks * 8 + g * 4);
+          const float4* tb = reinterpret_cast<const float4*>(qtab + (kTabA + (tl & 15)) * kTabStride + ks * 8 + g * 4);
+          const float4 a0 = ta[0], a1 = ta[1], b0 = tb[0], b1 = tb[1];
+          const float2 ca[4] = {make_float2(a0.x, a0.y), make_float2(a0.z, a0.w), make_float2(a1.x, a1.y),
+                                make_float2(a1.z, a1.w)};
+          const float2 cb[4] = {make_float2(b0.x, b0.y), make_float2(b0.z, b0.w), make_float2(b1.x, b1.y),
+                                make_float2(b1.z, b1.w)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)  // (sin, cos) of the sum of the two angles
+            sc[e] = make_float2(ca[e].x * cb[e].y + ca[e].y * cb[e].x, ca[e].y * cb[e].y - ca[e].x * cb[e].x);
         }
         u32x4 pk;
 #pragma unroll
@@ -665,12 +688,8 @@ void fwd_bf16_kernel(FwdParams p) {
           float x0 = bf16_lo(qraw[nb][ks][e]), x1 = bf16_hi(qraw[nb][ks][e]);
           if constexpr (ROPE) {
             float sn, cs;
-            if constexpr (kQTab) {
-              sn = sc[e].x;
-              cs = sc[e].y;
-            } else {
-              sincos_rev(rope_turns(pos + t, ropec_s[ks * 8 + g * 4 + e]), &sn, &cs);
-            }
+            sn = sc[e].x;
+            cs = sc[e].y;
             const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
             x0 = y0;
             x1 = y1;
