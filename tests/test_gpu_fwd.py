@@ -166,6 +166,22 @@ def test_gqa32k_every_work_item():
     check_close(f64(out)[idx], ro, "bf16", "gqa32k work items", f64(lse)[idx], rl)
 
 
+def test_gqa8k_keys_rotated_in_kernel_every_work_item():
+    """The 8192-token GQA workload with no workspace (each K block rotated as it lands, the
+    path a C caller without a workspace takes): one row of every work item, by the oracle."""
+    cfg = workloads.CONFIGS["gqa8k"]
+    say(f"workload gqa8k, keys rotated in the kernel: {cfg}")
+    q, k, v = gen(cfg)
+    out, lse = run_fwd_gpu(q, k, v, cfg["causal"], cfg["rope_base"], cfg["pos"], workspace=False)
+    assert bool(torch.isfinite(out).all()), "non-finite output"
+    rows = oracle_pool.work_item_rows(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], seed=cfg["seed"] + 1)
+    say(f"workload gqa8k: oracle on {len(rows)} rows")
+    ro, rl = oracle_pool.attention_rows_grouped(oracle_pool.f32(q), oracle_pool.f32(k), oracle_pool.f32(v), rows,
+                                                cfg["causal"], cfg["rope_base"], cfg["pos"])
+    idx = (rows[:, 0], rows[:, 1], rows[:, 2])
+    check_close(f64(out)[idx], ro, "bf16", "gqa8k work items (keys rotated in the kernel)", f64(lse)[idx], rl)
+
+
 @pytest.mark.parametrize("name", ["mha2k", "gqa8k", "gqa32k"])
 def test_full_workload_every_row_written(name):
     """Every (batch, head, row) of a full-size workload is produced by exactly one work item,
