@@ -24,10 +24,13 @@ def test_random_forward(c):
     q, k, v = workloads.make_fwd_inputs(B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], T=c["T"], S=c["S"], d_h=c["d_h"],
                                         dtype="bf16", seed=c["seed"])
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    # every other draw with a workspace for the keys rotated ahead, whatever the sizes
+    ws = torch.empty(kd.numel() * 2, dtype=torch.uint8, device="cuda") if c["seed"] % 2 else None
     if c["mode"] == "window":
-        out, lse = attn_fwd_window(qd, kd, vd, c["window"], rope_base=c["rope_base"], pos=c["pos"])
+        out, lse = attn_fwd_window(qd, kd, vd, c["window"], rope_base=c["rope_base"], pos=c["pos"], workspace=ws)
     else:
-        out, lse = attn_fwd(qd, kd, vd, causal=c["mode"] == "causal", rope_base=c["rope_base"], pos=c["pos"])
+        out, lse = attn_fwd(qd, kd, vd, causal=c["mode"] == "causal", rope_base=c["rope_base"], pos=c["pos"],
+                            workspace=ws)
     torch.cuda.synchronize()
     ro, rl = oracle.attention(f64(q), f64(k), f64(v), causal=c["mode"] != "full", rope_base=c["rope_base"],
                               pos=c["pos"], window=c["window"])
