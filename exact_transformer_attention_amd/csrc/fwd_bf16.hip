@@ -38,11 +38,15 @@
 //    before rounding to bf16, so p = exp2(s - m).
 //  * K and V move from HBM to LDS with direct 16-byte loads (global_load_lds_dwordx4),
 //    so no registers are tied up by loads in flight.  V lands in its final, xor-swizzled
-//    layout; raw K lands in a staging area and each thread rotates the chunks it loaded
-//    (RoPE at load) into the padded K tile.  The rotation angles advance from block to
-//    block by angle addition and are re-derived exactly (fp64 reduction) every 16 blocks.
-//  * Raw K is loaded two blocks ahead and V one block ahead; the rotation of block j+1
-//    happens during block j.  Work is ordered longest-first for causal load balance and
+//    layout.  K that needs no rotation here (keys rotated once ahead by rope_k_kernel, the
+//    paged cache's rotated keys, or no RoPE) lands straight in its padded operand tile;
+//    otherwise raw K lands in a staging area and each thread rotates the chunks it loaded
+//    (RoPE at load) into the padded K tile, with angles advanced from block to block by
+//    angle addition and re-derived exactly (fp64 reduction) every 16 blocks.  A K block is
+//    read by every query block of its group, so rotating it once ahead pays when those
+//    are many (the host decides, given a workspace).
+//  * V and direct K are loaded one block ahead; raw K two blocks ahead, the rotation of
+//    block j+1 happening during block j.  Work is ordered longest-first for causal load balance and
 //    mapped so all query blocks of one KV head land on one XCD; with enough query blocks
 //    per group the XCD runs its groups one after the other (one group's K/V in its L2 at
 //    a time), else it interleaves them longest first (work_order).
