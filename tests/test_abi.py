@@ -94,6 +94,50 @@ def kbytes(B, Hkv, S, d):
     return B * Hkv * S * d * 2
 
 
+def readers_per_key_block(Hq, Hkv, T, S, causal, window, pos):
+    """Brute force: over every workgroup of the bf16 prefill (HP heads x 256/HP rows), the key
+    blocks from the first its first row's window reaches to the last its last row sees;
+    summed, per KV head's key block."""
+    G = Hq // Hkv
+    HP = 4 if G % 4 == 0 else (2 if G % 2 == 0 else 1)
+    RH = 256 // HP
+    nkb = -(-S // 64)
+    reads = 0
+    for qb in range(-(-T // RH)):
+        last = min(T - 1, qb * RH + RH - 1)
+        nk = S if not causal else max(0, min(S, pos + last + 1))
+        first = 0
+        if window > 0:
+            lo = pos + qb * RH - window + 1
+            first = (0 if lo <= 0 else min(lo, nk)) // 64
+        reads += len(range(first, -(-nk // 64)))
+    return reads * (G // HP) / nkb
+
+
+def test_fwd_workspace_bytes_follows_the_reader_count(lib):
+    """Seeded shapes: the library asks for a workspace exactly when each key block is read by
+    at least 16 workgroups (brute-force count above)."""
+    import numpy as np
+    rng = np.random.default_rng(20261204)
+    asked = 0
+    for _ in range(300):
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        Hq = Hkv * int(rng.choice([1, 2, 3, 4, 8]))
+        T = int(rng.integers(1, 6000))
+        S = int(rng.integers(1, 6000))
+        causal = int(rng.integers(0, 2))
+        window = int(rng.choice([0, 0, int(rng.integers(1, 4000))]))
+        if window:
+            causal = 1
+        pos = int(rng.integers(-100, 3000)) if causal else 0
+        d = int(rng.choice([64, 128]))
+        got = lib.attn_fwd_workspace_bytes(1, Hq, Hkv, T, S, d, causal, window, 10000.0, pos, 1)
+        want = 1 * Hkv * S * d * 2 if readers_per_key_block(Hq, Hkv, T, S, causal, window, pos) >= 16 else 0
+        assert got == want, (Hq, Hkv, T, S, causal, window, pos, d)
+        asked += got > 0
+    assert 0 < asked < 300
+
+
 @pytest.mark.parametrize("args,expect", [
     # 2 x 32 query heads over 8 KV heads, 8192 causal tokens, RoPE: each K block is read by
     # about 64 workgroups of 4 heads x 64 rows -> rotate once ahead
