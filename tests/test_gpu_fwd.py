@@ -106,6 +106,12 @@ def test_bf16_workspace_use():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(o3, o4) and torch.equal(l3, l4)
     assert attn_fwd_workspace_bytes(1, 8, 2, 700, 700, 128, True, 0, 10000.0, 0) == 0
+    # fp32 inputs ignore a workspace (no rotated copy is made for the fp32 path)
+    qf, kf, vf = q.float(), k.float(), v.float()
+    f1 = attn_fwd(qf, kf, vf, causal=True, rope_base=10000.0, workspace=ws)
+    f2 = attn_fwd(qf, kf, vf, causal=True, rope_base=10000.0, workspace=False)
+    torch.cuda.synchronize()
+    assert torch.equal(f1[0], f2[0]) and torch.equal(f1[1], f2[1])
     ro, rl = oracle.attention(f64(q), f64(k), f64(v), causal=True, rope_base=10000.0, pos=0)
     check_close(f64(o1), ro, "bf16", "out (rotated ahead)", f64(l1), rl)
     check_close(f64(o3), ro, "bf16", "out (rotated in the prefill)", f64(l3), rl)

@@ -64,6 +64,20 @@ def test_window_keys_rotated_ahead(case):
     check_close(f64(out), ro, dtype, f"window {w}", f64(lse), rl)
 
 
+def test_window_covering_everything_equals_causal_keys_rotated_ahead():
+    """With the keys rotated ahead as well: a window reaching back past key 0 gives exactly
+    the causal call's result (the same rotated copy, the same kernel)."""
+    from exact_transformer_attention_amd import attn_fwd, attn_fwd_window
+    cfg = dict(B=1, Hq=8, Hkv=2, T=333, S=333, d_h=128, dtype="bf16", seed=32)
+    q, k, v = (x.cuda() for x in gen(cfg))
+    ws = torch.empty(k.numel() * 2, dtype=torch.uint8, device="cuda")
+    a = attn_fwd(q, k, v, causal=True, rope_base=10000.0, workspace=ws)
+    for w in (333, 5000):
+        b = attn_fwd_window(q, k, v, w, rope_base=10000.0, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), w
+
+
 def test_window_covering_everything_equals_causal():
     """A window reaching back past key 0 must give exactly the causal kernel's result."""
     from exact_transformer_attention_amd import attn_fwd
