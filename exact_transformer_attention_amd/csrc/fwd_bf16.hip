@@ -495,6 +495,38 @@ void fwd_bf16_kernel(FwdParams p) {
     }
   };
 
+  // ---- epilogue: O = o / l, lse = (m + log2 l) ln 2.  Waves whose last key block comes
+  // before the workgroup's last one (rows that end earlier on the causal diagonal) run it
+  // right after the workgroup's last barrier, so their stores drain while the other waves
+  // compute that block; no later wait holds the workgroup for them.
+  auto computes = [&](int it) {  // whether this wave has keys in block it
+    const int k0 = it * kBN;
+    return k0 < nk_wave && (int64_t)(k0 + kBN) > lo_wave;
+  };
+  auto finish = [&]() {
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const float lt = l_run[nb] + __shfl_xor(l_run[nb], 32);
+      const int t = wrow0 + nb * 32 + l32;
+      if (t < T) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        __bf16* og = (__bf16*)p.out + (((size_t)b * p.Hq + hq) * (size_t)T + t) * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            u32x2 w;
+            w[0] = pack_bf16(o[db][nb][4 * q4 + 0] * inv, o[db][nb][4 * q4 + 1] * inv);
+            w[1] = pack_bf16(o[db][nb][4 * q4 + 2] * inv, o[db][nb][4 * q4 + 3] * inv);
+            *(u32x2*)(og + db * 32 + q4 * 8 + g * 4) = w;
+          }
+        if (p.lse && g == 0)
+          p.lse[((size_t)b * p.Hq + hq) * (size_t)T + t] =
+              lt > 0.f ? (m_ref[nb] + __log2f(lt)) * kLn2 : -INFINITY;
+      }
+    }
+  };
+
   // ---- one block of keys.  PAR = it & 1 is a compile-time constant so that the LDS
   // buffers read (Ks[PAR], Vs[PAR]) and written (Ks[PAR ^ 1], Kraw[PAR], Vs[PAR ^ 1]) are
   // provably distinct and the scheduler may interleave the rotation of block it+1 with
@@ -521,7 +553,8 @@ void fwd_bf16_kernel(FwdParams p) {
     const int k0 = it * kBN;
     const __bf16* kbuf = ks_tile(par);
     const char* vbuf = (const char*)&Vs[PAR][0];
-    if (k0 < nk_wave && (int64_t)(k0 + kBN) > lo_wave) {
+    if (it == n_tiles - 1 && !computes(it)) finish();
+    if (computes(it)) {
       f32x16 s[2][kNB];
       // The rotation of block it+1 is woven into the product; after the last block it
       // rotates stale data into a buffer nobody reads.
@@ -728,28 +761,9 @@ void fwd_bf16_kernel(FwdParams p) {
     if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
-  // ---- epilogue: O = o / l, lse = (m + log2 l) ln 2.
-#pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    const float lt = l_run[nb] + __shfl_xor(l_run[nb], 32);
-    const int t = wrow0 + nb * 32 + l32;
-    if (t < T) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      __bf16* og = (__bf16*)p.out + (((size_t)b * p.Hq + hq) * (size_t)T + t) * D;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          u32x2 w;
-          w[0] = pack_bf16(o[db][nb][4 * q4 + 0] * inv, o[db][nb][4 * q4 + 1] * inv);
-          w[1] = pack_bf16(o[db][nb][4 * q4 + 2] * inv, o[db][nb][4 * q4 + 3] * inv);
-          *(u32x2*)(og + db * 32 + q4 * 8 + g * 4) = w;
-        }
-      if (p.lse && g == 0)
-        p.lse[((size_t)b * p.Hq + hq) * (size_t)T + t] =
-            lt > 0.f ? (m_ref[nb] + __log2f(lt)) * kLn2 : -INFINITY;
-    }
-  }
+  // ---- epilogue (finish, above).  A wave with no key in the workgroup's last block wrote
+  // its rows at the start of that block.
+  if (it0 >= n_tiles || computes(n_tiles - 1)) finish();
 }
 
 namespace {
