@@ -120,4 +120,21 @@ __host__ __device__ constexpr int work_order_mode(int nblk, int n_groups) {
   return (n_groups % 8) ? 0 : (nblk >= kSeqOrderMin ? 2 : 1);
 }
 
+// Writes one 32-dim block of a row held in the 32x32 accumulator layout: lane (row, g) holds
+// dims 8*q4 + 4*g + 0..3 of the block as w[q4] (four bf16).  One exchange with the lane 32
+// apart (the same row) gives lane g = 0 the 8 dims of q4 = 0 and 2 and lane g = 1 those of
+// q4 = 1 and 3, so each lane writes two 16-byte pieces (dst 16-byte aligned).  Both lanes of
+// a row must execute it.
+__device__ __forceinline__ void store_block_bf16(__bf16* dst, const u32x2 (&w)[4], int g) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {  // q4 pair (2h, 2h + 1)
+    const u32x2 send = g ? w[2 * h] : w[2 * h + 1];
+    u32x2 recv;
+    recv[0] = (uint32_t)__shfl_xor((int)send[0], 32);
+    recv[1] = (uint32_t)__shfl_xor((int)send[1], 32);
+    const u32x2 lo = g ? recv : w[2 * h], hi = g ? w[2 * h + 1] : recv;
+    *(u32x4*)(dst + (2 * h + g) * 8) = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+  }
+}
+
 }  // namespace attn

@@ -456,14 +456,13 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
     __bf16* dkg = (__bf16*)p.dk + (kvrow0 + key) * kD;
     const float isd = kLn2;
 #pragma unroll
-    for (int db = 0; db < kDB; ++db)
+    for (int db = 0; db < kDB; ++db) {
+      u32x2 wv[4], wk[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = db * 32 + q4 * 8 + g * 4;
-        u32x2 w;
-        w[0] = pack_bf16(dv[db][4 * q4 + 0], dv[db][4 * q4 + 1]);
-        w[1] = pack_bf16(dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]);
-        *(u32x2*)(dvg + d0) = w;
+        wv[q4][0] = pack_bf16(dv[db][4 * q4 + 0], dv[db][4 * q4 + 1]);
+        wv[q4][1] = pack_bf16(dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]);
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = dk[db][4 * q4 + e] * isd;
@@ -471,10 +470,12 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkdv_kernel(BwdParams p) {
           unrotate(x[0], x[1], rope_turns((int64_t)key, p.rope_c[d0 / 2]));
           unrotate(x[2], x[3], rope_turns((int64_t)key, p.rope_c[d0 / 2 + 1]));
         }
-        w[0] = pack_bf16(x[0], x[1]);
-        w[1] = pack_bf16(x[2], x[3]);
-        *(u32x2*)(dkg + d0) = w;
+        wk[q4][0] = pack_bf16(x[0], x[1]);
+        wk[q4][1] = pack_bf16(x[2], x[3]);
       }
+      store_block_bf16(dvg + db * 32, wv, g);  // 16-byte pieces
+      store_block_bf16(dkg + db * 32, wk, g);
+    }
   }
 }
 
@@ -683,7 +684,8 @@ void bwd_dq_kernel(BwdParams p) {
     __bf16* dqg = (__bf16*)p.dq + row * kD;
     const float isd = 1.f / sqrtf((float)kD);
 #pragma unroll
-    for (int db = 0; db < kDB; ++db)
+    for (int db = 0; db < kDB; ++db) {
+      u32x2 w[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = db * 32 + q4 * 8 + g * 4;
@@ -694,11 +696,11 @@ void bwd_dq_kernel(BwdParams p) {
           unrotate(x[0], x[1], rope_turns(pos + t, p.rope_c[d0 / 2]));
           unrotate(x[2], x[3], rope_turns(pos + t, p.rope_c[d0 / 2 + 1]));
         }
-        u32x2 w;
-        w[0] = pack_bf16(x[0], x[1]);
-        w[1] = pack_bf16(x[2], x[3]);
-        *(u32x2*)(dqg + d0) = w;
+        w[q4][0] = pack_bf16(x[0], x[1]);
+        w[q4][1] = pack_bf16(x[2], x[3]);
       }
+      store_block_bf16(dqg + db * 32, w, g);  // 16-byte pieces
+    }
   }
 }
 

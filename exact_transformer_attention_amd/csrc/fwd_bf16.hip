@@ -511,9 +511,6 @@ void fwd_bf16_kernel(FwdParams p) {
       if (t < T) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         __bf16* og = (__bf16*)p.out + (((size_t)b * p.Hq + hq) * (size_t)T + t) * D;
-        // Lane (row, g) holds dims db*32 + 8*q4 + 4*g + 0..3; one exchange with the lane 32
-        // apart (same row) gives lane g = 0 the 8 dims of q4 = 0 and 2, lane g = 1 those of
-        // q4 = 1 and 3, so each lane writes 16-byte pieces.
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           u32x2 w[4];
@@ -522,15 +519,7 @@ void fwd_bf16_kernel(FwdParams p) {
             w[q4][0] = pack_bf16(o[db][nb][4 * q4 + 0] * inv, o[db][nb][4 * q4 + 1] * inv);
             w[q4][1] = pack_bf16(o[db][nb][4 * q4 + 2] * inv, o[db][nb][4 * q4 + 3] * inv);
           }
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {  // q4 pair (2h, 2h + 1)
-            const u32x2 send = g ? w[2 * h] : w[2 * h + 1];
-            u32x2 recv;
-            recv[0] = (uint32_t)__shfl_xor((int)send[0], 32);
-            recv[1] = (uint32_t)__shfl_xor((int)send[1], 32);
-            const u32x2 lo = g ? recv : w[2 * h], hi = g ? w[2 * h + 1] : recv;
-            *(u32x4*)(og + db * 32 + (2 * h + g) * 8) = (u32x4){lo[0], lo[1], hi[0], hi[1]};
-          }
+          store_block_bf16(og + db * 32, w, g);  // 16-byte pieces
         }
         if (p.lse && g == 0)
           p.lse[((size_t)b * p.Hq + hq) * (size_t)T + t] =

@@ -292,14 +292,15 @@ void fwd_fp8_kernel(FwdParams p) {
     const float inv = lsum > 0.f ? p.v_scale / lsum : 0.f;
     __bf16* og = (__bf16*)p.out + (((size_t)b * p.Hq + hq) * (size_t)T + t) * kDim;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db) {
+      u32x2 w[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        u32x2 w;
-        w[0] = pack_bf16(o[db][4 * q4 + 0] * inv, o[db][4 * q4 + 1] * inv);
-        w[1] = pack_bf16(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
-        *(u32x2*)(og + db * 32 + q4 * 8 + g * 4) = w;
+        w[q4][0] = pack_bf16(o[db][4 * q4 + 0] * inv, o[db][4 * q4 + 1] * inv);
+        w[q4][1] = pack_bf16(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
       }
+      store_block_bf16(og + db * 32, w, g);  // 16-byte pieces
+    }
     if (p.lse && g == 0)
       p.lse[((size_t)b * p.Hq + hq) * (size_t)T + t] = lsum > 0.f ? (m_ref + __log2f(lsum)) * kLn2 : -INFINITY;
   }
