@@ -294,6 +294,58 @@ def cpu_baseline_config(name, cfg):
                 sample=f"{sample}, fp64 numpy, 1024-row blocks; {flops:.3e} FLOP (exact visible pairs)")
 
 
+def sweep_bench(a):
+    """bf16 prefill throughput across shapes (one JSON line with a row per shape): 32 query
+    heads, 32/16/8/4 KV heads, T = S from 1024 to 16384 tokens (batch 16384 / T), causal with
+    RoPE (base 1e4), non-causal at 4096, d_h = 128 and 64; seeded N(0, 1) inputs rounded to bf16,
+    the keys rotated ahead whenever attn_fwd_workspace_bytes asks for it.  Each shape is timed
+    with HIP events over --steps calls after at least 0.25 s of warm-up calls (the clocks settle
+    within that)."""
+    import torch
+    from exact_transformer_attention_amd import attn_fwd
+    rows = []
+    for d in (128, 64):
+        for hkv in (32, 16, 8, 4):
+            for T in (1024, 2048, 4096, 8192, 16384):
+                if d == 64 and T not in (2048, 8192):
+                    continue
+                B = max(1, 16384 // T)
+                for causal in ((True, False) if T == 4096 else (True,)):
+                    g = torch.Generator(device="cpu").manual_seed(T + hkv + d)
+                    q = torch.randn(B, 32, T, d, generator=g).to(torch.bfloat16).cuda()
+                    k = torch.randn(B, hkv, T, d, generator=g).to(torch.bfloat16).cuda()
+                    v = torch.randn(B, hkv, T, d, generator=g).to(torch.bfloat16).cuda()
+                    out = torch.empty_like(q)
+                    lse = torch.empty(B, 32, T, device="cuda")
+
+                    def run():
+                        attn_fwd(q, k, v, causal=causal, rope_base=10000.0, out=out, lse=lse)
+
+                    t0 = time.perf_counter()
+                    n = 0
+                    while n < a.warmup or time.perf_counter() - t0 < 0.25:
+                        run()
+                        torch.cuda.synchronize()
+                        n += 1
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(a.steps):
+                        run()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ms = e0.elapsed_time(e1) / a.steps
+                    flop = 4.0 * B * 32 * T * T * d / (2 if causal else 1)
+                    tf = flop / (ms * 1e-3) / 1e12
+                    rows.append({"B": B, "Hq": 32, "Hkv": hkv, "T": T, "d_h": d, "causal": causal,
+                                 "ms": round(ms, 4), "tflops": round(tf, 1),
+                                 "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+                    print(f"[bench] sweep {rows[-1]}", file=sys.stderr, flush=True)
+                    del q, k, v, out, lse
+    print(json.dumps({"metric": "bf16 prefill TFLOP/s across shapes", "unit": "TFLOP/s", "n_gpus": 1,
+                      "steps": a.steps, "warmup": "at least 0.25 s", "dtype": "bf16",
+                      "data": "synthetic (seeded iid normal, bf16-rounded)", "sweep": rows}))
+
+
 def config_bench(a, name):
     """Causal prefill of one of the other contiguous workloads (the 2048-token MHA shape or the
     32768-token GQA shape), timed like the headline prefill (one JSON line)."""
@@ -577,13 +629,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "decode", "window", "prefix", "bwd", "fp8", "mha2k", "gqa32k"],
+    ap.add_argument("--only", choices=["prefill", "decode", "window", "prefix", "bwd", "fp8", "mha2k", "gqa32k",
+                                       "sweep"],
                     default=None,
                     help="time only one part (profiling runs); 'window' times the causal sliding-window "
                          "prefill (attn_fwd_window) on the same 8192-token GQA workload instead; 'prefix' "
                          "the paged prefill (attn_prefill_paged) of 8 sequences over a shared 6144-token prefix; "
                          "'bwd' the backward (attn_bwd) of the 8192-token GQA prefill; 'fp8' the fp8 prefill "
-                         "(attn_fwd_fp8) on the same shape")
+                         "(attn_fwd_fp8) on the same shape; 'sweep' the bf16 prefill over a grid of shapes")
     ap.add_argument("--window", type=int, default=4096, help="window of --only window (keys)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/traffic.json "
@@ -614,6 +667,9 @@ def main():
         return
     if a.only in ("mha2k", "gqa32k"):
         config_bench(a, a.only)
+        return
+    if a.only == "sweep":
+        sweep_bench(a)
         return
 
     import torch
